@@ -1,0 +1,223 @@
+/*
+ * oases_shard.h -- C ABI of liboases_shard: one GPU's tensor-model-parallel
+ * (TMP) shard of a stack of attention / FFN blocks, run through the
+ * overlapped training schedule with fine-grained recomputation of
+ * "Oases: Efficient Large-Scale Model Training on Commodity Servers via
+ * Overlapped and Automated Tensor Model Parallelism" (arXiv 2305.16121),
+ * Section IV.
+ *
+ * Block l (a Megatron-style shard):
+ *   attention: QKV = X W_in^T + b_in      (W_in [3a, h], columns [Q | K | V],
+ *                                          each head-major, a = n_s * d)
+ *              O   = causal softmax(Q K^T / sqrt(d)) V      per (sequence, head)
+ *              P   = O W_out^T            (W_out [h, a])
+ *   FFN:       U = X W_in^T + b_in,  H = gelu(U) = U * Phi(U)   (W_in [f_s, h])
+ *              P = H W_out^T              (W_out [h, f_s])
+ *   AllReduce point C(F):  Y = P + sum_{k=1}^{w-1} peer_k   (Section IV: the
+ *              AllReduce output is the sum of its w inputs).  On one GPU the
+ *              w-1 peer partials are caller-provided resident buffers that
+ *              stand in for the other ranks.  Accumulated in float32 in the
+ *              order own, peer_1, ..., peer_{w-1}; rounded once to the
+ *              storage type (bf16: round to nearest even).
+ *   X_{l+1} = Y_l.  Backward: dP = dY (Eq. (1): the gradient of each
+ *              AllReduce input equals the gradient of its output), and the
+ *              backward AllReduce point C(B) sums this shard's dX with the
+ *              w-1 backward peer partials.
+ *
+ * Schedules (Section IV, Fig. 4, Algorithm 1): the batch is split along its
+ * batch dimension into two sub-batches (rows [0, T_sb) and [T_sb, 2 T_sb) of
+ * every [B*s, h] tensor, T_sb = (B/2) s).  Only block inputs are stored
+ * between forward and backward (checkpoints); the backward of block l and
+ * sub-batch sb is R (recompute from the stored input; the row GEMM is not
+ * re-run and C(R) is not issued), B_dX, C(B) (started asynchronously),
+ * B_dW.  Weight gradients: sub-batch 0 writes, sub-batch 1 accumulates.
+ *
+ * Conventions
+ *  - All tensors are row-major and dense.  Token row r = b*s + t.
+ *  - Storage type: float32 (OASES_F32) or bf16 (OASES_BF16) for activations,
+ *    weights and biases; weight and bias gradients are always float32.
+ *    Accumulation is float32 throughout.
+ *  - Pointers are device pointers, 16-byte aligned, owned by the caller.  The
+ *    library never allocates or frees device memory; it owns only HIP events
+ *    and graphs it creates.  Streams are borrowed (hipStream_t as void*).
+ *  - Every call returns an oases_status; nothing aborts or throws across the
+ *    ABI.  On failure oases_last_error() holds a message.  Argument checks run
+ *    before any HIP call, so a call that fails validation enqueues nothing.
+ *  - All enqueueing calls are asynchronous on the bound streams; only
+ *    oases_sync blocks the host.  One context belongs to one host thread.
+ */
+#ifndef OASES_SHARD_H
+#define OASES_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct oases_ctx oases_ctx; /* opaque; created by oases_create */
+
+typedef enum {
+  OASES_OK = 0,
+  OASES_E_ARG = -1,         /* bad argument: null pointer, index out of range */
+  OASES_E_STATE = -2,       /* call out of order (e.g. backward before forward) */
+  OASES_E_SHAPE = -3,       /* configuration the kernels do not support */
+  OASES_E_ALIGN = -4,       /* pointer not 16-byte aligned */
+  OASES_E_HIP = -5,         /* a HIP runtime call failed; see oases_last_error */
+  OASES_E_UNSUPPORTED = -6  /* valid request that this build does not implement */
+} oases_status;
+
+typedef enum { OASES_F32 = 0, OASES_BF16 = 1 } oases_dtype;
+typedef enum { OASES_ATTN = 0, OASES_FFN = 1 } oases_block;
+
+/* Step schedules (Section IV, Fig. 4).  OVERLAP_FINE issues every AllReduce
+ * point on the side stream so that one sub-batch's sum overlaps the other
+ * sub-batch's compute; the SERIAL modes issue everything on the compute
+ * stream.  DEFAULT_RECOMPUTE recomputes the whole block including its row
+ * GEMM and issues C(R) (its result is discarded); NO_RECOMPUTE keeps every
+ * block's intermediates from the forward pass (needs a larger workspace). */
+typedef enum {
+  OASES_OVERLAP_FINE = 0,
+  OASES_SERIAL_FINE = 1,
+  OASES_SERIAL_DEFAULT_RECOMPUTE = 2,
+  OASES_SERIAL_NO_RECOMPUTE = 3
+} oases_mode;
+
+/* Shape of the shard.  Constraints (OASES_E_SHAPE otherwise):
+ *   n_layers in [1, 64]; blocks[l] in {OASES_ATTN, OASES_FFN};
+ *   micro_batch >= 2 and even; seq >= 1;
+ *   hidden, ffn_shard multiples of 64; tmp_width >= 1;
+ *   attention blocks: head_dim in {64, 128}, heads_per_shard >= 1,
+ *   and dtype OASES_BF16 (float32 attention is OASES_E_UNSUPPORTED);
+ *   causal in {0, 1}.  The blocks array is copied by oases_create. */
+typedef struct {
+  int32_t n_layers;
+  const int32_t *blocks;
+  int32_t micro_batch, seq, hidden;
+  int32_t heads_per_shard, head_dim, ffn_shard, tmp_width;
+  int32_t dtype;   /* oases_dtype */
+  int32_t causal;
+} oases_config;
+
+/* Per-layer parameters.  N_in = 3a (attention) or f_s (FFN); N_mid = a or f_s.
+ *   w_in [N_in, h], b_in [N_in], w_out [h, N_mid]           storage type
+ *   dw_in [N_in, h], db_in [N_in], dw_out [h, N_mid]         float32, written
+ *   (overwritten by sub-batch 0, accumulated by sub-batch 1 of each step). */
+typedef struct {
+  const void *w_in, *b_in, *w_out;
+  void *dw_in, *db_in, *dw_out;
+} oases_layer_params;
+
+/* Activation buffers (storage type unless stated):
+ *   x   [B*s, h]   input of layer 0 (read only)
+ *   y   [B*s, h]   output of the top layer (written by its C(F))
+ *   dy  [B*s, h]   upstream gradient dL/dy (read only)
+ *   dx  [B*s, h]   gradient w.r.t. x (written by layer 0's C(B))
+ *   ckpt [L-1, B*s, h]  stored inputs of layers 1..L-1 (the only tensors kept
+ *        between forward and backward); may be NULL when L == 1
+ *   peers_fwd, peers_bwd [L, 2, w-1, T_sb, h]  resident peer partials of the
+ *        forward and backward AllReduce points, indexed [layer][sub-batch][k];
+ *        may be NULL when w == 1
+ *   workspace: device scratch of at least oases_workspace_bytes(cfg, mode)
+ *        bytes for every mode that will be run; 256-byte aligned. */
+typedef struct {
+  const void *x;
+  void *y;
+  const void *dy;
+  void *dx;
+  void *ckpt;
+  const void *peers_fwd, *peers_bwd;
+  void *workspace;
+  size_t workspace_bytes;
+} oases_buffers;
+
+/* Validate cfg and create a context.  Makes no HIP call. */
+int oases_create(const oases_config *cfg, oases_ctx **out);
+
+/* Workspace bytes needed by `mode` (NO_RECOMPUTE needs per-layer
+ * intermediates, the other modes one set per sub-batch).  No HIP call. */
+int oases_workspace_bytes(const oases_config *cfg, int32_t mode, size_t *bytes);
+
+/* Bind caller buffers and per_layer[n_layers] parameters.  Checks non-null
+ * and 16-byte alignment of every pointer that the configuration needs.
+ * Resets the per-step state.  No HIP call. */
+int oases_bind(oases_ctx *c, const oases_buffers *b, const oases_layer_params *per_layer);
+
+/* Borrow the compute stream and the side (communication) stream; NULL means
+ * the default stream.  Passing the same stream twice serialises everything.
+ * Creates the context's HIP events on the current device. */
+int oases_set_streams(oases_ctx *c, void *compute_stream, void *side_stream);
+
+/* Forward operator of block `layer` for sub-batch `sub_batch` (0 or 1):
+ * F on the compute stream (waiting for the C(F) that produced its input),
+ * then StartAsync of C(F) on the side stream.  Requires layer_fwd of
+ * (layer-1, sub_batch) earlier in the step.  Intermediates are not kept. */
+int layer_fwd(oases_ctx *c, int32_t layer, int32_t sub_batch);
+
+/* Fine-grained backward of block `layer`, sub-batch `sub_batch`: R (recompute
+ * from the stored input, no row GEMM, no C(R)), then B_dX after a Sync on the
+ * C(B) of (layer+1, sub_batch), StartAsync of C(B) on the side stream, then
+ * B_dW on the compute stream.  Requires layer_fwd of the top layer for this
+ * sub-batch and layer_bwd_recompute of (layer+1, sub_batch); sub-batch 1 of a
+ * layer requires sub-batch 0 of the same layer first (gradient accumulation
+ * order).  Otherwise OASES_E_STATE. */
+int layer_bwd_recompute(oases_ctx *c, int32_t layer, int32_t sub_batch);
+
+/* One whole step (forward + backward of every layer and both sub-batches) in
+ * `mode`.  use_graph != 0 captures the step into a hipGraph on its first
+ * call per mode and replays it afterwards. */
+int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph);
+
+/* Op list of `mode` as issued by schedule_step, four int32 per op:
+ * kind (0 F, 1 C_F, 2 R, 3 C_R, 4 B_dX, 5 C_B, 6 B_dW), layer, sub-batch,
+ * stream (0 compute, 1 side).  Writes at most `cap` ops, returns the count in
+ * *n_ops.  No HIP call. */
+int oases_schedule_ops(const oases_ctx *c, int32_t mode, int32_t *ops, int32_t cap,
+                       int32_t *n_ops);
+
+/* Block the host until both bound streams are idle. */
+int oases_sync(oases_ctx *c);
+
+/* Last error message of the context ("" if none); valid until the next call. */
+const char *oases_last_error(const oases_ctx *c);
+
+/* Release events and graphs.  Safe on NULL. */
+void oases_destroy(oases_ctx *c);
+
+/* Timing instrumentation of one kernel class (0 GEMM forward/recompute,
+ * 1 GEMM data gradient, 2 GEMM weight gradient, 3 attention forward,
+ * 4 attention backward, 5 AllReduce-point sum, 6 bias-gradient column sum).
+ * After oases_profile_begin, every eager (not graph-captured) launch of that
+ * class is bracketed by HIP events on the stream it is launched on, for at
+ * most max_launches launches.  oases_profile_end waits for those events and
+ * returns the summed kernel time and the number of launches timed. */
+int oases_profile_begin(oases_ctx *c, int32_t kernel_class, int32_t max_launches);
+int oases_profile_end(oases_ctx *c, double *total_ms, int32_t *launches);
+
+/* ---- single-kernel entry points (used by tests and the benchmark) ----
+ * They run one kernel family on `stream` (NULL = default) with the same
+ * device code as the step, so each kernel can be checked and timed alone. */
+
+/* AllReduce-point sum (Section IV): out[i] = own[i] + sum_k peers[k*peer_stride + i]
+ * for i < n, float32 accumulation in that order, one rounding to dtype.
+ * n_peers >= 0; n a multiple of 8. */
+int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int64_t peer_stride,
+                          int32_t n_peers, void *out, int64_t n, void *stream);
+
+/* C[M,N] = A[M,K] B[N,K]^T (+ bias[N]), optional exact GeLU: act = 0 none,
+ * 1 gelu (writes gelu(acc+bias) to c and, if pre != NULL, acc+bias to pre).
+ * Storage-type operands; K, N multiples of 8; lda/ldb/ldc in elements. */
+int oases_gemm_fwd(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *a, int32_t lda,
+                   const void *b, int32_t ldb, const void *bias, int32_t act, void *c,
+                   int32_t ldc, void *pre, void *stream);
+
+/* Causal attention forward over [nb*s, 3a] QKV -> O [nb*s, a] and log-sum-exp
+ * lse [nb, n_h, s] (float32, natural log).  bf16 only; d in {64, 128}. */
+int oases_attention_fwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t causal,
+                        const void *qkv, void *o, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OASES_SHARD_H */

@@ -1,0 +1,141 @@
+// Bandwidth-bound kernels: the AllReduce-point sum and the deterministic
+// column sum used for bias gradients.
+#include "common.h"
+#include "kernels.h"
+
+namespace oases {
+namespace {
+
+// ---------------------------------------------------------------------------
+// AllReduce point (Oases, Section IV: the AllReduce output is the sum of its
+// w inputs).  out = own + peer_1 + ... + peer_{w-1}, float32 adds in that
+// order, one rounding to the storage type.  Each thread streams 8 elements
+// (16 bytes of bf16) per input per iteration, so every input read is one
+// coalesced 16-byte load and the w loads of an iteration are in flight
+// together.
+// ---------------------------------------------------------------------------
+constexpr int SUM_NT = 256;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// streaming 16-byte load that bypasses cache retention (each byte is read once)
+__device__ __forceinline__ uint4 stream_load(const uint4 *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__global__ void __launch_bounds__(SUM_NT)
+    allreduce_bf16_kernel(const uint4 *__restrict__ own, const bf16_t *__restrict__ peers,
+                          int64_t peer_stride, int n_peers, uint4 *__restrict__ out, int64_t nvec) {
+  for (int64_t v = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v < nvec;
+       v += (int64_t)gridDim.x * SUM_NT) {
+    const uint4 a = stream_load(own + v);
+    float acc[8] = {lo_f32(a.x), hi_f32(a.x), lo_f32(a.y), hi_f32(a.y),
+                    lo_f32(a.z), hi_f32(a.z), lo_f32(a.w), hi_f32(a.w)};
+    for (int k = 0; k < n_peers; ++k) {
+      const uint4 b = stream_load(reinterpret_cast<const uint4 *>(peers + (int64_t)k * peer_stride) + v);
+      acc[0] += lo_f32(b.x); acc[1] += hi_f32(b.x);
+      acc[2] += lo_f32(b.y); acc[3] += hi_f32(b.y);
+      acc[4] += lo_f32(b.z); acc[5] += hi_f32(b.z);
+      acc[6] += lo_f32(b.w); acc[7] += hi_f32(b.w);
+    }
+    out[v] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  }
+}
+
+__global__ void __launch_bounds__(SUM_NT)
+    allreduce_f32_kernel(const float4 *__restrict__ own, const float *__restrict__ peers,
+                         int64_t peer_stride, int n_peers, float4 *__restrict__ out, int64_t nvec) {
+  for (int64_t v = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v < nvec;
+       v += (int64_t)gridDim.x * SUM_NT) {
+    float4 acc = own[v];
+    for (int k = 0; k < n_peers; ++k) {
+      const float4 b = reinterpret_cast<const float4 *>(peers + (int64_t)k * peer_stride)[v];
+      acc.x += b.x; acc.y += b.y; acc.z += b.z; acc.w += b.w;
+    }
+    out[v] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Column sums, two passes with a fixed order (no atomics):
+//   pass 1: partial[chunk][c] = sum of rows [chunk*64, chunk*64+64) of column c
+//   pass 2: db[c] = (beta ? db[c] : 0) + sum over chunks in increasing order
+// ---------------------------------------------------------------------------
+constexpr int CS_ROWS = 64;
+
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+    colsum_pass1(const void *__restrict__ x, int rows, int cols, int ldx, float *__restrict__ partial) {
+  const int c8 = (blockIdx.x * 256 + threadIdx.x) * 8;  // 8 consecutive columns per thread
+  const int chunk = blockIdx.y;
+  if (c8 >= cols) return;
+  float acc[8] = {};
+  const int r1 = min(rows, (chunk + 1) * CS_ROWS);
+  for (int r = chunk * CS_ROWS; r < r1; ++r) {
+    if constexpr (BF16) {
+      const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(x) + (int64_t)r * ldx + c8);
+      acc[0] += lo_f32(a.x); acc[1] += hi_f32(a.x); acc[2] += lo_f32(a.y); acc[3] += hi_f32(a.y);
+      acc[4] += lo_f32(a.z); acc[5] += hi_f32(a.z); acc[6] += lo_f32(a.w); acc[7] += hi_f32(a.w);
+    } else {
+      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)r * ldx + c8);
+      const float4 a = p[0], b = p[1];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+  }
+  float4 *o = reinterpret_cast<float4 *>(partial + (int64_t)chunk * cols + c8);
+  o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+__global__ void __launch_bounds__(256)
+    colsum_pass2(const float *__restrict__ partial, int nchunks, int cols, float *__restrict__ db, int beta) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  float acc = beta ? db[c] : 0.f;
+  for (int ch = 0; ch < nchunks; ++ch) acc += partial[(int64_t)ch * cols + c];
+  db[c] = acc;
+}
+
+}  // namespace
+
+hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
+                           int n_peers, void *out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t per_vec = bf16 ? 8 : 4;
+  const int64_t nvec = n / per_vec;
+  const int64_t want = (nvec + SUM_NT - 1) / SUM_NT;
+  const int grid = (int)(want < 2048 ? want : 2048);
+  if (bf16)
+    hipLaunchKernelGGL(allreduce_bf16_kernel, dim3(grid), dim3(SUM_NT), 0, s,
+                       static_cast<const uint4 *>(own), static_cast<const bf16_t *>(peers),
+                       peer_stride, n_peers, static_cast<uint4 *>(out), nvec);
+  else
+    hipLaunchKernelGGL(allreduce_f32_kernel, dim3(grid), dim3(SUM_NT), 0, s,
+                       static_cast<const float4 *>(own), static_cast<const float *>(peers),
+                       peer_stride, n_peers, static_cast<float4 *>(out), nvec);
+  return hipGetLastError();
+}
+
+int64_t colsum_partial_floats(int rows, int cols) {
+  return (int64_t)((rows + CS_ROWS - 1) / CS_ROWS) * cols;
+}
+
+hipError_t colsum(bool bf16, const void *x, int rows, int cols, int ldx, float *partial, float *db,
+                  int beta, hipStream_t s) {
+  if (cols <= 0) return hipSuccess;
+  const int nchunks = (rows + CS_ROWS - 1) / CS_ROWS;
+  if (nchunks > 0) {
+    dim3 g1((cols / 8 + 255) / 256, nchunks);
+    if (bf16)
+      hipLaunchKernelGGL(colsum_pass1<true>, g1, dim3(256), 0, s, x, rows, cols, ldx, partial);
+    else
+      hipLaunchKernelGGL(colsum_pass1<false>, g1, dim3(256), 0, s, x, rows, cols, ldx, partial);
+  }
+  hipLaunchKernelGGL(colsum_pass2, dim3((cols + 255) / 256), dim3(256), 0, s, partial, nchunks,
+                     cols, db, beta);
+  return hipGetLastError();
+}
+
+}  // namespace oases

@@ -1,0 +1,715 @@
+// liboases_shard: context, validation, workspace layout, the op lists of the
+// four step schedules and their issue on a compute and a side HIP stream,
+// hipGraph capture, and the C-ABI entry points.
+//
+// Schedule source: "Oases: Efficient Large-Scale Model Training on Commodity
+// Servers via Overlapped and Automated Tensor Model Parallelism"
+// (arXiv 2305.16121), Section IV: the batch split into two sub-batches whose
+// operators pipeline (Fig. 4b); fine-grained recomputation that starts after
+// the forward communication operator and drops C(R) (Eq. (1), Fig. 4d); the
+// runtime executor whose computation operators have Forward / Recompute /
+// Backward and whose communication operators have StartAsync / Sync, storing
+// only the input of each recompute sequence (Algorithm 1).  StartAsync here is
+// "record an event on the compute stream, make the side stream wait on it,
+// launch the AllReduce-point kernel on the side stream, record its event";
+// Sync is "make the compute stream wait on that event".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/oases_shard.h"
+#include "kernels.h"
+
+using namespace oases;
+
+namespace {
+
+enum OpKind : int32_t { OP_F = 0, OP_CF = 1, OP_R = 2, OP_CR = 3, OP_BDX = 4, OP_CB = 5, OP_BDW = 6 };
+struct Op {
+  int32_t kind, layer, sb, stream;
+};
+
+// kernel classes for timing instrumentation
+enum KClass : int32_t {
+  KC_GEMM_FWD = 0, KC_GEMM_DX = 1, KC_GEMM_DW = 2, KC_ATTN_FWD = 3, KC_ATTN_BWD = 4,
+  KC_SUM = 5, KC_COLSUM = 6, KC_COUNT = 7
+};
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Dims {
+  int L, B, s, h, ns, d, fs, w, dtype, causal;
+  int T, a, nb;  // tokens per sub-batch, attention width, sequences per sub-batch
+  size_t esz;
+  bool any_attn, any_ffn;
+  std::vector<int32_t> blocks;
+  int n_in(int l) const { return blocks[l] == OASES_ATTN ? 3 * a : fs; }
+  int n_mid(int l) const { return blocks[l] == OASES_ATTN ? a : fs; }
+  int max_n_in() const { return std::max(any_attn ? 3 * a : 0, any_ffn ? fs : 0); }
+};
+
+// workspace layout for one mode (byte offsets)
+struct WsLayout {
+  size_t P[2], dxo[2], dpre[2], dO[2], delta[2];
+  size_t act_bytes;      // one activation slot
+  size_t act0;           // first slot; slot (i, sb) at act0 + (i*2 + sb) * act_bytes
+  int n_slots;
+  // offsets inside a slot
+  size_t s_U, s_H, s_QKV, s_O, s_LSE;
+  size_t colsum;
+  size_t gbuf[2];
+  size_t cr_out;
+  size_t total;
+};
+
+WsLayout make_layout(const Dims &D, int mode) {
+  WsLayout o{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t r = off; off = align_up(off + bytes); return r; };
+  const size_t th = (size_t)D.T * D.h * D.esz;
+  const size_t lse_bytes = (size_t)D.nb * D.ns * D.s * sizeof(float);
+  for (int sb = 0; sb < 2; ++sb) {
+    o.P[sb] = take(th);
+    o.dxo[sb] = take(th);
+    o.dpre[sb] = take((size_t)D.T * D.max_n_in() * D.esz);
+    o.dO[sb] = D.any_attn ? take((size_t)D.T * D.a * D.esz) : 0;
+    o.delta[sb] = D.any_attn ? take(lse_bytes) : 0;
+  }
+  // activation slot: FFN {U, H} or attention {QKV, O, LSE}; slot size is the max
+  size_t ffn_sz = 0, attn_sz = 0;
+  if (D.any_ffn) ffn_sz = 2 * align_up((size_t)D.T * D.fs * D.esz);
+  if (D.any_attn)
+    attn_sz = align_up((size_t)D.T * 3 * D.a * D.esz) + align_up((size_t)D.T * D.a * D.esz) +
+              align_up(lse_bytes);
+  o.act_bytes = align_up(std::max(ffn_sz, attn_sz));
+  o.s_U = 0;
+  o.s_H = D.any_ffn ? align_up((size_t)D.T * D.fs * D.esz) : 0;
+  o.s_QKV = 0;
+  o.s_O = D.any_attn ? align_up((size_t)D.T * 3 * D.a * D.esz) : 0;
+  o.s_LSE = D.any_attn ? o.s_O + align_up((size_t)D.T * D.a * D.esz) : 0;
+  o.n_slots = (mode == OASES_SERIAL_NO_RECOMPUTE) ? D.L : 1;
+  o.act0 = take(o.act_bytes * 2 * o.n_slots);
+  o.colsum = take((size_t)colsum_partial_floats(D.T, D.max_n_in()) * sizeof(float));
+  if (D.L > 1) {
+    o.gbuf[0] = take((size_t)2 * th);
+    o.gbuf[1] = take((size_t)2 * th);
+  }
+  o.cr_out = (mode == OASES_SERIAL_DEFAULT_RECOMPUTE) ? take(th) : 0;
+  o.total = off;
+  return o;
+}
+
+int check_config(const oases_config *cfg, Dims *D, std::string *err) {
+  auto fail = [&](int code, const char *msg) { if (err) *err = msg; return code; };
+  if (!cfg) return fail(OASES_E_ARG, "config is NULL");
+  if (cfg->n_layers < 1 || cfg->n_layers > 64) return fail(OASES_E_SHAPE, "n_layers must be in [1, 64]");
+  if (!cfg->blocks) return fail(OASES_E_ARG, "blocks is NULL");
+  if (cfg->dtype != OASES_F32 && cfg->dtype != OASES_BF16) return fail(OASES_E_ARG, "bad dtype");
+  if (cfg->micro_batch < 2 || cfg->micro_batch % 2) return fail(OASES_E_SHAPE, "micro_batch must be even and >= 2");
+  if (cfg->seq < 1) return fail(OASES_E_SHAPE, "seq must be >= 1");
+  if (cfg->hidden < 64 || cfg->hidden % 64) return fail(OASES_E_SHAPE, "hidden must be a positive multiple of 64");
+  if (cfg->tmp_width < 1) return fail(OASES_E_SHAPE, "tmp_width must be >= 1");
+  if (cfg->causal != 0 && cfg->causal != 1) return fail(OASES_E_ARG, "causal must be 0 or 1");
+  Dims d{};
+  d.L = cfg->n_layers;
+  d.blocks.assign(cfg->blocks, cfg->blocks + cfg->n_layers);
+  for (int32_t b : d.blocks) {
+    if (b == OASES_ATTN) d.any_attn = true;
+    else if (b == OASES_FFN) d.any_ffn = true;
+    else return fail(OASES_E_ARG, "block kind must be OASES_ATTN or OASES_FFN");
+  }
+  if (d.any_ffn && (cfg->ffn_shard < 64 || cfg->ffn_shard % 64))
+    return fail(OASES_E_SHAPE, "ffn_shard must be a positive multiple of 64");
+  if (d.any_attn) {
+    if (cfg->head_dim != 64 && cfg->head_dim != 128) return fail(OASES_E_SHAPE, "head_dim must be 64 or 128");
+    if (cfg->heads_per_shard < 1) return fail(OASES_E_SHAPE, "heads_per_shard must be >= 1");
+    if (cfg->dtype != OASES_BF16) return fail(OASES_E_UNSUPPORTED, "attention blocks need bf16 storage");
+  }
+  const int64_t T = (int64_t)(cfg->micro_batch / 2) * cfg->seq;
+  if (T * (int64_t)cfg->hidden >= (int64_t(1) << 31) || T * 3LL * cfg->heads_per_shard * cfg->head_dim >= (int64_t(1) << 31) ||
+      T * (int64_t)cfg->ffn_shard >= (int64_t(1) << 31))
+    return fail(OASES_E_SHAPE, "a sub-batch tensor exceeds 2^31 elements");
+  d.B = cfg->micro_batch; d.s = cfg->seq; d.h = cfg->hidden;
+  d.ns = d.any_attn ? cfg->heads_per_shard : 0;
+  d.d = d.any_attn ? cfg->head_dim : 0;
+  d.fs = d.any_ffn ? cfg->ffn_shard : 0;
+  d.w = cfg->tmp_width; d.dtype = cfg->dtype; d.causal = cfg->causal;
+  d.T = (int)T; d.a = d.ns * d.d; d.nb = d.B / 2;
+  d.esz = cfg->dtype == OASES_BF16 ? 2 : 4;
+  if (D) *D = std::move(d);
+  return OASES_OK;
+}
+
+std::vector<Op> build_ops(int L, int mode) {
+  std::vector<Op> ops;
+  const int side = mode == OASES_OVERLAP_FINE ? 1 : 0;
+  for (int l = 0; l < L; ++l)
+    for (int sb = 0; sb < 2; ++sb) {
+      ops.push_back({OP_F, l, sb, 0});
+      ops.push_back({OP_CF, l, sb, side});
+    }
+  for (int l = L - 1; l >= 0; --l)
+    for (int sb = 0; sb < 2; ++sb) {
+      if (mode != OASES_SERIAL_NO_RECOMPUTE) ops.push_back({OP_R, l, sb, 0});
+      if (mode == OASES_SERIAL_DEFAULT_RECOMPUTE) ops.push_back({OP_CR, l, sb, 0});
+      ops.push_back({OP_BDX, l, sb, 0});
+      ops.push_back({OP_CB, l, sb, side});
+      ops.push_back({OP_BDW, l, sb, 0});
+    }
+  return ops;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+struct oases_ctx {
+  Dims D;
+  bool bound = false;
+  oases_buffers buf{};
+  std::vector<oases_layer_params> prm;
+  hipStream_t cs = nullptr, ss = nullptr;
+  bool streams_set = false;
+  std::vector<hipEvent_t> evF, evCF, evBdX, evCB;
+  hipGraphExec_t gexec[4] = {nullptr, nullptr, nullptr, nullptr};
+  std::vector<uint8_t> fwd_done, bwd_done;
+  std::string err;
+  // timing instrumentation
+  int prof_class = -1;
+  std::vector<hipEvent_t> prof_ev;
+  size_t prof_used = 0;
+  bool capturing = false;
+};
+
+namespace {
+
+int set_err(oases_ctx *c, int code, const std::string &msg) {
+  if (c) c->err = msg;
+  return code;
+}
+
+#define HIPX(expr)                                                                      \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return set_err(c, OASES_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+void destroy_graphs(oases_ctx *c) {
+  for (auto &g : c->gexec)
+    if (g) { (void)hipGraphExecDestroy(g); g = nullptr; }
+}
+
+// ---- the executor: one op at a time --------------------------------------
+
+struct Exec {
+  oases_ctx *c;
+  const WsLayout &W;
+  int mode;
+  bool overlap;  // side stream distinct from the compute stream
+
+  char *ws() const { return static_cast<char *>(c->buf.workspace); }
+  const Dims &D() const { return c->D; }
+  size_t th_bytes() const { return (size_t)D().T * D().h * D().esz; }
+  bool bf16() const { return D().dtype == OASES_BF16; }
+
+  const char *layer_in(int l, int sb) const {
+    const char *base = l == 0 ? static_cast<const char *>(c->buf.x)
+                              : static_cast<const char *>(c->buf.ckpt) + (size_t)(l - 1) * 2 * th_bytes();
+    return base + sb * th_bytes();
+  }
+  char *layer_out(int l, int sb) const {
+    char *base = l == D().L - 1 ? static_cast<char *>(c->buf.y)
+                                : static_cast<char *>(c->buf.ckpt) + (size_t)l * 2 * th_bytes();
+    return base + sb * th_bytes();
+  }
+  // gradient w.r.t. the output of layer l (read by its backward)
+  const char *grad_out(int l, int sb) const {
+    const char *base = l == D().L - 1 ? static_cast<const char *>(c->buf.dy) : ws() + W.gbuf[l % 2];
+    return base + sb * th_bytes();
+  }
+  // gradient w.r.t. the input of layer l (written by its C(B))
+  char *grad_in(int l, int sb) const {
+    char *base = l == 0 ? static_cast<char *>(c->buf.dx) : ws() + W.gbuf[(l - 1) % 2];
+    return base + sb * th_bytes();
+  }
+  char *slot(int l, int sb) const {
+    const int i = W.n_slots == 1 ? 0 : l;
+    return ws() + W.act0 + (size_t)(i * 2 + sb) * W.act_bytes;
+  }
+  const char *peers(const void *p, int l, int sb) const {
+    const size_t per = (size_t)(D().w - 1) * th_bytes();
+    return static_cast<const char *>(p) + (size_t)(l * 2 + sb) * per;
+  }
+
+  int prof_begin(int cls, hipStream_t s) {
+    if (c->prof_class != cls || c->capturing) return OASES_OK;
+    if (c->prof_used + 2 > c->prof_ev.size()) return OASES_OK;  // ring full: stop timing
+    HIPX(hipEventRecord(c->prof_ev[c->prof_used], s));
+    return OASES_OK;
+  }
+  int prof_end(int cls, hipStream_t s) {
+    if (c->prof_class != cls || c->capturing) return OASES_OK;
+    if (c->prof_used + 2 > c->prof_ev.size()) return OASES_OK;
+    HIPX(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
+    c->prof_used += 2;
+    return OASES_OK;
+  }
+
+  int gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmArgs &g, hipStream_t s);
+  int sum(const void *own, const void *pr, void *out, hipStream_t s) {
+    if (int r = prof_begin(KC_SUM, s)) return r;
+    HIPX(allreduce_point(bf16(), own, pr, (int64_t)D().T * D().h, D().w - 1, out, (int64_t)D().T * D().h, s));
+    return prof_end(KC_SUM, s);
+  }
+
+  // column part of block l (F or R): writes the slot's activations.
+  int column_part(int l, int sb, bool keep_pre) {
+    const Dims &d = D();
+    const oases_layer_params &p = c->prm[l];
+    char *sl = slot(l, sb);
+    const void *x = layer_in(l, sb);
+    if (d.blocks[l] == OASES_FFN) {
+      GemmArgs g{};
+      g.M = d.T; g.N = d.fs; g.K = d.h;
+      g.A = x; g.lda = d.h; g.B = p.w_in; g.ldb = d.h;
+      g.C = sl + W.s_H; g.ldc = d.fs; g.bias = p.b_in;
+      g.pre = keep_pre ? sl + W.s_U : nullptr; g.ld_pre = d.fs;
+      return gemm(KC_GEMM_FWD, KC, KC, EPI_BIAS_GELU, g, c->cs);
+    }
+    GemmArgs g{};
+    g.M = d.T; g.N = 3 * d.a; g.K = d.h;
+    g.A = x; g.lda = d.h; g.B = p.w_in; g.ldb = d.h;
+    g.C = sl + W.s_QKV; g.ldc = 3 * d.a; g.bias = p.b_in;
+    if (int r = gemm(KC_GEMM_FWD, KC, KC, EPI_BIAS, g, c->cs)) return r;
+    if (int r = prof_begin(KC_ATTN_FWD, c->cs)) return r;
+    HIPX(attention_fwd(d.nb, d.s, d.ns, d.d, d.causal, sl + W.s_QKV, sl + W.s_O,
+                       reinterpret_cast<float *>(sl + W.s_LSE), c->cs));
+    return prof_end(KC_ATTN_FWD, c->cs);
+  }
+
+  // row-parallel GEMM of block l: partial P[sb] = act W_out^T
+  int row_part(int l, int sb) {
+    const Dims &d = D();
+    const oases_layer_params &p = c->prm[l];
+    char *sl = slot(l, sb);
+    GemmArgs g{};
+    g.M = d.T; g.N = d.h; g.K = d.n_mid(l);
+    g.A = d.blocks[l] == OASES_FFN ? sl + W.s_H : sl + W.s_O; g.lda = d.n_mid(l);
+    g.B = p.w_out; g.ldb = d.n_mid(l);
+    g.C = ws() + W.P[sb]; g.ldc = d.h;
+    return gemm(KC_GEMM_FWD, KC, KC, EPI_STORE, g, c->cs);
+  }
+
+  int op_F(int l, int sb) {
+    if (overlap && l > 0) HIPX(hipStreamWaitEvent(c->cs, c->evCF[(l - 1) * 2 + sb], 0));
+    const bool keep = mode == OASES_SERIAL_NO_RECOMPUTE;
+    if (int r = column_part(l, sb, keep)) return r;
+    if (int r = row_part(l, sb)) return r;
+    if (overlap) HIPX(hipEventRecord(c->evF[l * 2 + sb], c->cs));
+    return OASES_OK;
+  }
+  int op_CF(int l, int sb) {
+    hipStream_t s = overlap ? c->ss : c->cs;
+    if (overlap) HIPX(hipStreamWaitEvent(s, c->evF[l * 2 + sb], 0));
+    if (int r = sum(ws() + W.P[sb], D().w > 1 ? peers(c->buf.peers_fwd, l, sb) : nullptr,
+                    layer_out(l, sb), s))
+      return r;
+    if (overlap) HIPX(hipEventRecord(c->evCF[l * 2 + sb], s));
+    return OASES_OK;
+  }
+  int op_R(int l, int sb) {
+    if (int r = column_part(l, sb, true)) return r;
+    if (mode == OASES_SERIAL_DEFAULT_RECOMPUTE) return row_part(l, sb);
+    return OASES_OK;
+  }
+  int op_CR(int l, int sb) {
+    return sum(ws() + W.P[sb], D().w > 1 ? peers(c->buf.peers_fwd, l, sb) : nullptr, ws() + W.cr_out, c->cs);
+  }
+  int op_BdX(int l, int sb) {
+    const Dims &d = D();
+    const oases_layer_params &p = c->prm[l];
+    if (overlap && l < d.L - 1) HIPX(hipStreamWaitEvent(c->cs, c->evCB[(l + 1) * 2 + sb], 0));
+    char *sl = slot(l, sb);
+    const void *dy = grad_out(l, sb);
+    char *dpre = ws() + W.dpre[sb];
+    if (d.blocks[l] == OASES_FFN) {
+      GemmArgs g{};  // dU = (dY W_out) * gelu'(U)
+      g.M = d.T; g.N = d.fs; g.K = d.h;
+      g.A = dy; g.lda = d.h; g.B = p.w_out; g.ldb = d.fs;
+      g.C = dpre; g.ldc = d.fs; g.aux = sl + W.s_U; g.ld_aux = d.fs;
+      if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_GELU_BWD, g, c->cs)) return r;
+    } else {
+      GemmArgs g{};  // dO = dY W_o
+      g.M = d.T; g.N = d.a; g.K = d.h;
+      g.A = dy; g.lda = d.h; g.B = p.w_out; g.ldb = d.a;
+      g.C = ws() + W.dO[sb]; g.ldc = d.a;
+      if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_STORE, g, c->cs)) return r;
+      if (int r = prof_begin(KC_ATTN_BWD, c->cs)) return r;
+      HIPX(attention_bwd(d.nb, d.s, d.ns, d.d, d.causal, sl + W.s_QKV, sl + W.s_O, ws() + W.dO[sb],
+                         reinterpret_cast<const float *>(sl + W.s_LSE),
+                         reinterpret_cast<float *>(ws() + W.delta[sb]), dpre, c->cs));
+      if (int r = prof_end(KC_ATTN_BWD, c->cs)) return r;
+    }
+    GemmArgs g{};  // dX_own = dpre W_in
+    g.M = d.T; g.N = d.h; g.K = d.n_in(l);
+    g.A = dpre; g.lda = d.n_in(l); g.B = p.w_in; g.ldb = d.h;
+    g.C = ws() + W.dxo[sb]; g.ldc = d.h;
+    if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_STORE, g, c->cs)) return r;
+    if (overlap) HIPX(hipEventRecord(c->evBdX[l * 2 + sb], c->cs));
+    return OASES_OK;
+  }
+  int op_CB(int l, int sb) {
+    hipStream_t s = overlap ? c->ss : c->cs;
+    if (overlap) HIPX(hipStreamWaitEvent(s, c->evBdX[l * 2 + sb], 0));
+    if (int r = sum(ws() + W.dxo[sb], D().w > 1 ? peers(c->buf.peers_bwd, l, sb) : nullptr,
+                    grad_in(l, sb), s))
+      return r;
+    if (overlap) HIPX(hipEventRecord(c->evCB[l * 2 + sb], s));
+    return OASES_OK;
+  }
+  int op_BdW(int l, int sb) {
+    const Dims &d = D();
+    const oases_layer_params &p = c->prm[l];
+    char *sl = slot(l, sb);
+    const void *dy = grad_out(l, sb);
+    const char *dpre = ws() + W.dpre[sb];
+    const int nmid = d.n_mid(l), nin = d.n_in(l);
+    GemmArgs g{};  // dW_out[h, nmid] (+)= dY^T act
+    g.M = d.h; g.N = nmid; g.K = d.T;
+    g.A = dy; g.lda = d.h;
+    g.B = d.blocks[l] == OASES_FFN ? sl + W.s_H : sl + W.s_O; g.ldb = nmid;
+    g.C = p.dw_out; g.ldc = nmid; g.beta = sb;
+    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g, c->cs)) return r;
+    GemmArgs g2{};  // dW_in[nin, h] (+)= dpre^T X
+    g2.M = nin; g2.N = d.h; g2.K = d.T;
+    g2.A = dpre; g2.lda = nin; g2.B = layer_in(l, sb); g2.ldb = d.h;
+    g2.C = p.dw_in; g2.ldc = d.h; g2.beta = sb;
+    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, c->cs)) return r;
+    if (int r = prof_begin(KC_COLSUM, c->cs)) return r;
+    HIPX(colsum(bf16(), dpre, d.T, nin, nin, reinterpret_cast<float *>(ws() + W.colsum),
+                static_cast<float *>(p.db_in), sb, c->cs));
+    return prof_end(KC_COLSUM, c->cs);
+  }
+
+  int run(const Op &o) {
+    switch (o.kind) {
+      case OP_F: return op_F(o.layer, o.sb);
+      case OP_CF: return op_CF(o.layer, o.sb);
+      case OP_R: return op_R(o.layer, o.sb);
+      case OP_CR: return op_CR(o.layer, o.sb);
+      case OP_BDX: return op_BdX(o.layer, o.sb);
+      case OP_CB: return op_CB(o.layer, o.sb);
+      case OP_BDW: return op_BdW(o.layer, o.sb);
+    }
+    return set_err(c, OASES_E_ARG, "bad op");
+  }
+};
+
+int Exec::gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmArgs &g, hipStream_t s) {
+  if (int r = prof_begin(cls, s)) return r;
+  if (bf16()) HIPX(gemm_bf16(la, lb, epi, g, s));
+  else HIPX(gemm_f32(la, lb, epi, g, s));
+  return prof_end(cls, s);
+}
+
+int ensure_events(oases_ctx *c) {
+  if (!c->evF.empty()) return OASES_OK;
+  const int n = c->D.L * 2;
+  for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB}) {
+    v->resize(n, nullptr);
+    for (auto &e : *v) HIPX(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  }
+  return OASES_OK;
+}
+
+int need_ready(oases_ctx *c, int mode) {
+  if (!c->bound) return set_err(c, OASES_E_STATE, "buffers are not bound");
+  if (!c->streams_set) return set_err(c, OASES_E_STATE, "streams are not set");
+  const WsLayout W = make_layout(c->D, mode);
+  if (c->buf.workspace_bytes < W.total)
+    return set_err(c, OASES_E_ARG, "workspace too small for this mode: need " + std::to_string(W.total) +
+                                       " bytes");
+  return OASES_OK;
+}
+
+int issue_ops(oases_ctx *c, int mode, const std::vector<Op> &ops) {
+  const WsLayout W = make_layout(c->D, mode);
+  Exec ex{c, W, mode, mode == OASES_OVERLAP_FINE && c->ss != c->cs};
+  for (const Op &o : ops)
+    if (int r = ex.run(o)) return r;
+  if (ex.overlap) {  // join the side stream into the compute stream
+    HIPX(hipStreamWaitEvent(c->cs, c->evCB[0 * 2 + 1], 0));
+  }
+  return OASES_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+int oases_create(const oases_config *cfg, oases_ctx **out) {
+  if (!out) return OASES_E_ARG;
+  *out = nullptr;
+  Dims d;
+  std::string err;
+  const int r = check_config(cfg, &d, &err);
+  if (r) {
+    std::fprintf(stderr, "oases_create: %s\n", err.c_str());
+    return r;
+  }
+  oases_ctx *c = new oases_ctx();
+  c->D = std::move(d);
+  c->fwd_done.assign(c->D.L * 2, 0);
+  c->bwd_done.assign(c->D.L * 2, 0);
+  *out = c;
+  return OASES_OK;
+}
+
+int oases_workspace_bytes(const oases_config *cfg, int32_t mode, size_t *bytes) {
+  if (!bytes) return OASES_E_ARG;
+  if (mode < 0 || mode > 3) return OASES_E_ARG;
+  Dims d;
+  if (int r = check_config(cfg, &d, nullptr)) return r;
+  *bytes = make_layout(d, mode).total;
+  return OASES_OK;
+}
+
+int oases_bind(oases_ctx *c, const oases_buffers *b, const oases_layer_params *per_layer) {
+  if (!c) return OASES_E_ARG;
+  if (!b || !per_layer) return set_err(c, OASES_E_ARG, "buffers or per_layer is NULL");
+  const Dims &D = c->D;
+  struct P { const void *p; const char *name; bool need; };
+  const P ps[] = {{b->x, "x", true}, {b->y, "y", true}, {b->dy, "dy", true}, {b->dx, "dx", true},
+                  {b->ckpt, "ckpt", D.L > 1}, {b->peers_fwd, "peers_fwd", D.w > 1},
+                  {b->peers_bwd, "peers_bwd", D.w > 1}, {b->workspace, "workspace", true}};
+  for (const P &p : ps) {
+    if (!p.need) continue;
+    if (!p.p) return set_err(c, OASES_E_ARG, std::string(p.name) + " is NULL");
+    if (!aligned16(p.p)) return set_err(c, OASES_E_ALIGN, std::string(p.name) + " is not 16-byte aligned");
+  }
+  if ((uintptr_t)b->workspace % ALIGN) return set_err(c, OASES_E_ALIGN, "workspace is not 256-byte aligned");
+  const size_t need = make_layout(D, OASES_SERIAL_FINE).total;
+  if (b->workspace_bytes < need)
+    return set_err(c, OASES_E_ARG, "workspace smaller than oases_workspace_bytes(OASES_SERIAL_FINE) = " +
+                                       std::to_string(need));
+  for (int l = 0; l < D.L; ++l) {
+    const oases_layer_params &q = per_layer[l];
+    const void *lp[] = {q.w_in, q.b_in, q.w_out, q.dw_in, q.db_in, q.dw_out};
+    const char *nm[] = {"w_in", "b_in", "w_out", "dw_in", "db_in", "dw_out"};
+    for (int i = 0; i < 6; ++i) {
+      if (!lp[i]) return set_err(c, OASES_E_ARG, "layer " + std::to_string(l) + " " + nm[i] + " is NULL");
+      if (!aligned16(lp[i]))
+        return set_err(c, OASES_E_ALIGN, "layer " + std::to_string(l) + " " + nm[i] + " is not 16-byte aligned");
+    }
+  }
+  destroy_graphs(c);
+  c->buf = *b;
+  c->prm.assign(per_layer, per_layer + D.L);
+  c->bound = true;
+  std::fill(c->fwd_done.begin(), c->fwd_done.end(), 0);
+  std::fill(c->bwd_done.begin(), c->bwd_done.end(), 0);
+  c->err.clear();
+  return OASES_OK;
+}
+
+int oases_set_streams(oases_ctx *c, void *compute_stream, void *side_stream) {
+  if (!c) return OASES_E_ARG;
+  if (int r = ensure_events(c)) return r;
+  destroy_graphs(c);
+  c->cs = static_cast<hipStream_t>(compute_stream);
+  c->ss = static_cast<hipStream_t>(side_stream);
+  c->streams_set = true;
+  return OASES_OK;
+}
+
+int layer_fwd(oases_ctx *c, int32_t layer, int32_t sub_batch) {
+  if (!c) return OASES_E_ARG;
+  if (layer < 0 || layer >= c->D.L) return set_err(c, OASES_E_ARG, "layer out of range");
+  if (sub_batch != 0 && sub_batch != 1) return set_err(c, OASES_E_ARG, "sub_batch must be 0 or 1");
+  if (!c->bound) return set_err(c, OASES_E_STATE, "buffers are not bound");
+  if (layer == 0 && sub_batch == 0) {  // a new step starts
+    std::fill(c->fwd_done.begin(), c->fwd_done.end(), 0);
+    std::fill(c->bwd_done.begin(), c->bwd_done.end(), 0);
+  }
+  if (layer > 0 && !c->fwd_done[(layer - 1) * 2 + sub_batch])
+    return set_err(c, OASES_E_STATE, "layer_fwd needs the previous layer's forward of this sub-batch");
+  if (c->fwd_done[layer * 2 + sub_batch]) return set_err(c, OASES_E_STATE, "layer_fwd already issued in this step");
+  if (int r = need_ready(c, OASES_SERIAL_FINE)) return r;
+  const WsLayout W = make_layout(c->D, OASES_SERIAL_FINE);
+  Exec ex{c, W, OASES_SERIAL_FINE, c->ss != c->cs};
+  if (int r = ex.op_F(layer, sub_batch)) return r;
+  if (int r = ex.op_CF(layer, sub_batch)) return r;
+  c->fwd_done[layer * 2 + sub_batch] = 1;
+  return OASES_OK;
+}
+
+int layer_bwd_recompute(oases_ctx *c, int32_t layer, int32_t sub_batch) {
+  if (!c) return OASES_E_ARG;
+  const int L = c->D.L;
+  if (layer < 0 || layer >= L) return set_err(c, OASES_E_ARG, "layer out of range");
+  if (sub_batch != 0 && sub_batch != 1) return set_err(c, OASES_E_ARG, "sub_batch must be 0 or 1");
+  if (!c->bound) return set_err(c, OASES_E_STATE, "buffers are not bound");
+  if (!c->fwd_done[(L - 1) * 2 + sub_batch])
+    return set_err(c, OASES_E_STATE, "backward before the forward of this sub-batch finished");
+  if (layer < L - 1 && !c->bwd_done[(layer + 1) * 2 + sub_batch])
+    return set_err(c, OASES_E_STATE, "backward needs the layer above first");
+  if (sub_batch == 1 && !c->bwd_done[layer * 2 + 0])
+    return set_err(c, OASES_E_STATE, "sub-batch 1 of a layer needs sub-batch 0 first (gradient order)");
+  if (c->bwd_done[layer * 2 + sub_batch]) return set_err(c, OASES_E_STATE, "backward already issued in this step");
+  if (int r = need_ready(c, OASES_SERIAL_FINE)) return r;
+  const WsLayout W = make_layout(c->D, OASES_SERIAL_FINE);
+  Exec ex{c, W, OASES_SERIAL_FINE, c->ss != c->cs};
+  if (int r = ex.op_R(layer, sub_batch)) return r;
+  if (int r = ex.op_BdX(layer, sub_batch)) return r;
+  if (int r = ex.op_CB(layer, sub_batch)) return r;
+  if (int r = ex.op_BdW(layer, sub_batch)) return r;
+  if (ex.overlap && layer == 0) HIPX(hipStreamWaitEvent(c->cs, c->evCB[sub_batch], 0));
+  c->bwd_done[layer * 2 + sub_batch] = 1;
+  return OASES_OK;
+}
+
+int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph) {
+  if (!c) return OASES_E_ARG;
+  if (mode < 0 || mode > 3) return set_err(c, OASES_E_ARG, "bad mode");
+  if (int r = need_ready(c, mode)) return r;
+  const std::vector<Op> ops = build_ops(c->D.L, mode);
+  std::fill(c->fwd_done.begin(), c->fwd_done.end(), 0);
+  std::fill(c->bwd_done.begin(), c->bwd_done.end(), 0);
+  if (!use_graph) return issue_ops(c, mode, ops);
+  if (!c->gexec[mode]) {
+    if (c->cs == nullptr) return set_err(c, OASES_E_ARG, "graph capture needs a non-default compute stream");
+    HIPX(hipStreamBeginCapture(c->cs, hipStreamCaptureModeThreadLocal));
+    c->capturing = true;
+    const int r = issue_ops(c, mode, ops);
+    c->capturing = false;
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(c->cs, &graph);
+    if (r) { if (graph) (void)hipGraphDestroy(graph); return r; }
+    if (e != hipSuccess) return set_err(c, OASES_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    const hipError_t e2 = hipGraphInstantiate(&c->gexec[mode], graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e2 != hipSuccess) {
+      c->gexec[mode] = nullptr;
+      return set_err(c, OASES_E_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e2));
+    }
+  }
+  HIPX(hipGraphLaunch(c->gexec[mode], c->cs));
+  return OASES_OK;
+}
+
+int oases_schedule_ops(const oases_ctx *c, int32_t mode, int32_t *ops, int32_t cap, int32_t *n_ops) {
+  if (!c || !n_ops || (cap > 0 && !ops) || cap < 0) return OASES_E_ARG;
+  if (mode < 0 || mode > 3) return OASES_E_ARG;
+  const std::vector<Op> v = build_ops(c->D.L, mode);
+  *n_ops = (int32_t)v.size();
+  for (int i = 0; i < (int)v.size() && i < cap; ++i) {
+    ops[4 * i + 0] = v[i].kind; ops[4 * i + 1] = v[i].layer;
+    ops[4 * i + 2] = v[i].sb; ops[4 * i + 3] = v[i].stream;
+  }
+  return OASES_OK;
+}
+
+int oases_sync(oases_ctx *c) {
+  if (!c) return OASES_E_ARG;
+  if (!c->streams_set) return set_err(c, OASES_E_STATE, "streams are not set");
+  HIPX(hipStreamSynchronize(c->cs));
+  if (c->ss != c->cs) HIPX(hipStreamSynchronize(c->ss));
+  return OASES_OK;
+}
+
+const char *oases_last_error(const oases_ctx *c) { return c ? c->err.c_str() : "NULL context"; }
+
+void oases_destroy(oases_ctx *c) {
+  if (!c) return;
+  destroy_graphs(c);
+  for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB, &c->prof_ev})
+    for (auto &e : *v)
+      if (e) (void)hipEventDestroy(e);
+  delete c;
+}
+
+// ---- timing instrumentation ----
+
+int oases_profile_begin(oases_ctx *c, int32_t kernel_class, int32_t max_launches) {
+  if (!c) return OASES_E_ARG;
+  if (kernel_class < 0 || kernel_class >= KC_COUNT || max_launches < 1 || max_launches > 1 << 16)
+    return set_err(c, OASES_E_ARG, "bad kernel class or launch count");
+  for (auto &e : c->prof_ev) if (e) (void)hipEventDestroy(e);
+  c->prof_ev.assign((size_t)max_launches * 2, nullptr);
+  for (auto &e : c->prof_ev) HIPX(hipEventCreate(&e));
+  c->prof_used = 0;
+  c->prof_class = kernel_class;
+  return OASES_OK;
+}
+
+int oases_profile_end(oases_ctx *c, double *total_ms, int32_t *launches) {
+  if (!c || !total_ms || !launches) return OASES_E_ARG;
+  double tot = 0;
+  for (size_t i = 0; i + 1 < c->prof_used; i += 2) {
+    HIPX(hipEventSynchronize(c->prof_ev[i + 1]));
+    float ms = 0;
+    HIPX(hipEventElapsedTime(&ms, c->prof_ev[i], c->prof_ev[i + 1]));
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int32_t)(c->prof_used / 2);
+  c->prof_class = -1;
+  c->prof_used = 0;
+  return OASES_OK;
+}
+
+// ---- single-kernel entry points ----
+
+int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int64_t peer_stride,
+                          int32_t n_peers, void *out, int64_t n, void *stream) {
+  if (dtype != OASES_F32 && dtype != OASES_BF16) return OASES_E_ARG;
+  if (n < 0 || n % 8 || n_peers < 0 || (n_peers > 0 && (!peers || peer_stride % 8))) return OASES_E_ARG;
+  if (n == 0) return OASES_OK;
+  if (!own || !out) return OASES_E_ARG;
+  if (!aligned16(own) || !aligned16(out) || (n_peers > 0 && !aligned16(peers))) return OASES_E_ALIGN;
+  const hipError_t e = allreduce_point(dtype == OASES_BF16, own, peers, peer_stride, n_peers, out, n,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? OASES_OK : OASES_E_HIP;
+}
+
+int oases_gemm_fwd(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *a, int32_t lda,
+                   const void *b, int32_t ldb, const void *bias, int32_t act, void *c_, int32_t ldc,
+                   void *pre, void *stream) {
+  if (dtype != OASES_F32 && dtype != OASES_BF16) return OASES_E_ARG;
+  if (m < 0 || n < 0 || k < 0 || n % 8 || k % 8 || (act != 0 && act != 1)) return OASES_E_ARG;
+  if (m == 0 || n == 0) return OASES_OK;
+  if (!a || !b || !c_ || (act == 1 && !bias)) return OASES_E_ARG;
+  if (lda < k || ldb < k || ldc < n || lda % 8 || ldb % 8 || ldc % 8) return OASES_E_ARG;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c_) || (pre && !aligned16(pre)) ||
+      (bias && ((uintptr_t)bias & 7)))
+    return OASES_E_ALIGN;
+  GemmArgs g{};
+  g.M = m; g.N = n; g.K = k; g.A = a; g.lda = lda; g.B = b; g.ldb = ldb; g.C = c_; g.ldc = ldc;
+  g.bias = bias; g.pre = pre; g.ld_pre = ldc;
+  const Epi epi = act == 1 ? EPI_BIAS_GELU : (bias ? EPI_BIAS : EPI_STORE);
+  const hipError_t e = dtype == OASES_BF16 ? gemm_bf16(KC, KC, epi, g, static_cast<hipStream_t>(stream))
+                                           : gemm_f32(KC, KC, epi, g, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? OASES_OK : OASES_E_HIP;
+}
+
+int oases_attention_fwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t causal, const void *qkv,
+                        void *o, float *lse, void *stream) {
+  if (nb < 0 || s < 0 || n_h < 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1)) return OASES_E_ARG;
+  if (nb == 0 || s == 0 || n_h == 0) return OASES_OK;
+  if (!qkv || !o || !lse) return OASES_E_ARG;
+  if (!aligned16(qkv) || !aligned16(o) || !aligned16(lse)) return OASES_E_ALIGN;
+  const hipError_t e = attention_fwd(nb, s, n_h, d, causal, qkv, o, lse, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? OASES_OK : OASES_E_HIP;
+}
+
+}  // extern "C"

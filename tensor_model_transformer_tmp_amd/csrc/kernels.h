@@ -1,0 +1,65 @@
+// Host-side launchers of the gfx950 kernels.  Every launcher enqueues on
+// `stream` and returns the hipError_t of the launch.  Shapes are checked by
+// the caller (executor / C-ABI entry points) before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oases {
+
+// GEMM epilogues
+enum Epi : int {
+  EPI_STORE = 0,      // C = acc                              (storage type)
+  EPI_BIAS = 1,       // C = acc + bias[n]
+  EPI_BIAS_GELU = 2,  // pre = acc + bias[n] (optional), C = gelu(acc + bias[n])
+  EPI_GELU_BWD = 3,   // C = acc * gelu'(aux[m][n])
+  EPI_F32 = 4         // C(float32) = acc (+ C if beta)
+};
+
+// Operand layouts: for A(m,k): KC = stored [M][lda] (k contiguous),
+// MC = stored [K][lda] (m contiguous).  For B(k,n): KC = stored [N][ldb]
+// (k contiguous), MC = stored [K][ldb] (n contiguous).
+enum Layout : int { KC = 0, MC = 1 };
+
+struct GemmArgs {
+  int M, N, K;
+  const void *A;
+  int lda;
+  const void *B;
+  int ldb;
+  void *C;
+  int ldc;
+  const void *bias;
+  void *pre;
+  int ld_pre;
+  const void *aux;
+  int ld_aux;
+  int beta;
+};
+
+// C[M,N] = sum_k A(m,k) B(k,n) with the given layouts and epilogue.
+// bf16 operands on MFMA; float32 operands on a SIMT kernel.
+hipError_t gemm_bf16(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream_t s);
+hipError_t gemm_f32(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream_t s);
+
+// AllReduce point: out = own + sum_k peers[k] (float32 accumulation in order)
+hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
+                           int n_peers, void *out, int64_t n, hipStream_t s);
+
+// db (+)= column sums of x[rows, cols] in a fixed order; partial needs
+// colsum_partial_floats(rows, cols) floats.
+int64_t colsum_partial_floats(int rows, int cols);
+hipError_t colsum(bool bf16, const void *x, int rows, int cols, int ldx, float *partial, float *db,
+                  int beta, hipStream_t s);
+
+// Causal attention over QKV [nb*s, 3a] (columns [Q | K | V], head-major):
+// O [nb*s, a], lse [nb, nh, s] (natural log).  bf16, d in {64, 128}.
+hipError_t attention_fwd(int nb, int s, int nh, int d, int causal, const void *qkv, void *o,
+                         float *lse, hipStream_t st);
+// Backward: delta[nb, nh, s] = rowsum(dO * O) workspace; writes dQKV [nb*s, 3a].
+hipError_t attention_bwd(int nb, int s, int nh, int d, int causal, const void *qkv,
+                         const void *o, const void *dout, const float *lse, float *delta,
+                         void *dqkv, hipStream_t st);
+
+}  // namespace oases

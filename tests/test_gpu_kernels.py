@@ -1,0 +1,104 @@
+"""Single-kernel parity on the GPU: the AllReduce-point sum (bit-exact against
+the storage-type oracle), the forward GEMM with bias / GeLU epilogues, and
+causal attention forward, against float64 definitions on the same inputs."""
+import math
+
+import numpy as np
+import pytest
+
+import gen
+from oracle import blocks, sums
+from helpers import assert_close, gpu_available
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import torch
+    from tensor_model_transformer_tmp_amd import shard
+    from tensor_model_transformer_tmp_amd.device import to_device, to_storage
+
+
+def _bf16_bits(rng, shape, std=1.0):
+    v = (rng.standard_normal(shape) * std).astype(np.float32)
+    return gen._f32_to_bf16_bits(v).reshape(shape)
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.F32])
+@pytest.mark.parametrize("n,n_peers", [(8, 1), (4096 * 8 + 24, 0), (4096 * 8 + 24, 3),
+                                        (1 << 20, 7), (3 * 2048 * 1024, 3)])
+def test_allreduce_point_bit_exact(dtype, n, n_peers):
+    rng = np.random.default_rng(n + n_peers)
+    mk = (lambda s: _bf16_bits(rng, s)) if dtype == gen.BF16 else \
+        (lambda s: rng.standard_normal(s).astype(np.float32))
+    own = mk((n,))
+    peers = mk((max(n_peers, 1), n))
+    dev = "cuda"
+    t_own, t_peers = to_device(own, dtype, dev), to_device(peers, dtype, dev)
+    out = torch.empty_like(t_own)
+    shard.allreduce_point(dtype, t_own, t_peers, n_peers, out)
+    torch.cuda.synchronize()
+    want = sums.allreduce_point_storage(own, [peers[k] for k in range(n_peers)], dtype == gen.BF16)
+    np.testing.assert_array_equal(to_storage(out), want)
+
+
+@pytest.mark.parametrize("m,n,k", [(200, 192, 128), (1000, 520, 576), (2048, 1024, 1024),
+                                   (4096, 3072, 512), (37, 8, 8)])
+@pytest.mark.parametrize("epi", ["store", "bias", "gelu"])
+def test_gemm_fwd_bf16(m, n, k, epi):
+    rng = np.random.default_rng(m * 7 + n + k)
+    a, w = _bf16_bits(rng, (m, k)), _bf16_bits(rng, (n, k), 0.05)
+    b = _bf16_bits(rng, (n,), 0.5)
+    dev = "cuda"
+    ta, tw, tb = (to_device(x, gen.BF16, dev) for x in (a, w, b))
+    c = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+    pre = torch.empty_like(c) if epi == "gelu" else None
+    shard.gemm_fwd(shard.BF16, ta, tw, c, bias=None if epi == "store" else tb,
+                   gelu=epi == "gelu", pre=pre)
+    torch.cuda.synchronize()
+    af, wf, bf = (gen.bf16_bits_to_f64(x) for x in (a, w, b))
+    ref = af @ wf.T + (0 if epi == "store" else bf)
+    if epi == "gelu":
+        assert_close(gen.bf16_bits_to_f64(to_storage(pre)), ref, 8e-3, "pre-activation")
+        ref = blocks.gelu(ref)
+    got = gen.bf16_bits_to_f64(to_storage(c))
+    assert_close(got, ref, 8e-3, f"C {m}x{n}x{k} {epi}")
+    np.testing.assert_allclose(got, ref, rtol=1.6e-2, atol=1e-2 * np.abs(ref).max())
+
+
+def test_gemm_fwd_f32():
+    rng = np.random.default_rng(5)
+    m, n, k = 77, 136, 64
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    b = rng.standard_normal(n).astype(np.float32)
+    ta, tw, tb = (torch.from_numpy(x).cuda() for x in (a, w, b))
+    c, pre = torch.empty(m, n, device="cuda"), torch.empty(m, n, device="cuda")
+    shard.gemm_fwd(shard.F32, ta, tw, c, bias=tb, gelu=True, pre=pre)
+    torch.cuda.synchronize()
+    ref = a.astype(np.float64) @ w.astype(np.float64).T + b
+    assert_close(pre.cpu().numpy(), ref, 1e-6, "pre")
+    assert_close(c.cpu().numpy(), blocks.gelu(ref), 1e-6, "gelu")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nb,s,nh,causal", [(1, 1, 1, True), (2, 100, 3, True), (1, 300, 2, False),
+                                            (2, 512, 2, True), (1, 1030, 1, True)])
+def test_attention_fwd(d, nb, s, nh, causal):
+    rng = np.random.default_rng(d + s + nh)
+    a = nh * d
+    qkv = _bf16_bits(rng, (nb * s, 3 * a))
+    t = to_device(qkv, gen.BF16, "cuda")
+    o = torch.empty(nb * s, a, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(nb, nh, s, dtype=torch.float32, device="cuda")
+    shard.attention_fwd(nb, s, nh, d, causal, t, o, lse)
+    torch.cuda.synchronize()
+    f = gen.bf16_bits_to_f64(qkv)
+    q, k, v = (blocks.split_heads(f[:, i * a:(i + 1) * a], nb, s, nh, d) for i in range(3))
+    o_ref, _ = blocks.attention_fwd(q, k, v, causal)
+    assert_close(gen.bf16_bits_to_f64(to_storage(o)), blocks.merge_heads(o_ref), 2e-2, "O")
+    sc = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(d)
+    if causal:
+        sc = np.where(np.triu(np.ones((s, s), bool), 1), -np.inf, sc)
+    mx = sc.max(-1, keepdims=True)
+    lse_ref = (mx + np.log(np.exp(sc - mx).sum(-1, keepdims=True)))[..., 0]
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-3)

@@ -1,0 +1,111 @@
+"""Whole-step parity on the GPU: every schedule of liboases_shard against the
+float64 oracle on the same seeded inputs (1e-5 for float32 storage, 2e-2 for
+bf16), bit-identity of the overlapped / graph / serial / default-recompute /
+no-recompute schedules, and the per-layer entry points against schedule_step."""
+import numpy as np
+import pytest
+
+import gen
+from oracle import schedule as oschedule
+from helpers import assert_close, gpu_available
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import torch
+    from tensor_model_transformer_tmp_amd.device import DeviceShard
+
+MODES = ("overlap_fine", "serial_fine", "serial_default", "serial_norecompute")
+
+# small bf16 stacks with ragged sizes (tokens, hidden, heads and widths that do
+# not fill a tile) and both head sizes
+SMALL = {
+    "pair_d64_ragged": gen.ShardConfig(name="pair_d64_ragged", blocks=(gen.ATTN, gen.FFN),
+                                       micro_batch=2, seq=100, hidden=192, heads_per_shard=3,
+                                       head_dim=64, ffn_shard=320, tmp_width=3, dtype=gen.BF16,
+                                       seed=7),
+    "pair_d128": gen.ShardConfig(name="pair_d128", blocks=(gen.ATTN, gen.FFN), micro_batch=4,
+                                 seq=160, hidden=256, heads_per_shard=2, head_dim=128,
+                                 ffn_shard=512, tmp_width=2, dtype=gen.BF16, seed=8),
+    "stack4_d64": gen.ShardConfig(name="stack4_d64", blocks=(gen.ATTN, gen.FFN) * 2,
+                                  micro_batch=2, seq=256, hidden=256, heads_per_shard=4,
+                                  head_dim=64, ffn_shard=384, tmp_width=4, dtype=gen.BF16,
+                                  seed=9),
+    "ffn_only_w1": gen.ShardConfig(name="ffn_only_w1", blocks=(gen.FFN,), micro_batch=2, seq=64,
+                                   hidden=128, heads_per_shard=1, head_dim=64, ffn_shard=256,
+                                   tmp_width=1, dtype=gen.BF16, seed=10),
+}
+
+
+def _compare(cfg, got, ref, tol):
+    dec = lambda a: gen.storage_to_f64(a, cfg.dtype)
+    assert_close(dec(got["Y"]), ref["Y"], tol, f"{cfg.name} Y")
+    assert_close(dec(got["dX"]), ref["dX"], tol, f"{cfg.name} dX")
+    for l in range(cfg.n_layers):
+        for n in ("dw_in", "db_in", "dw_out"):
+            assert_close(got["grads"][l][n], ref["grads"][l][n], tol, f"{cfg.name} layer {l} {n}")
+
+
+def _bitwise_equal(a, b):
+    np.testing.assert_array_equal(a["Y"], b["Y"])
+    np.testing.assert_array_equal(a["dX"], b["dX"])
+    for ga, gb in zip(a["grads"], b["grads"]):
+        for n in ga:
+            np.testing.assert_array_equal(ga[n], gb[n], err_msg=n)
+
+
+@pytest.mark.parametrize("zero_peers", [False, True])
+def test_fp32_ffn_block_all_modes(zero_peers):
+    cfg = gen.PRESETS["c1_ffn_fp32"]
+    inp = gen.make_inputs(cfg, zero_peers=zero_peers)
+    ref = oschedule.run_step(inp, "serial_fine")
+    dev = DeviceShard(inp)
+    for mode in MODES:
+        dev.step(mode)
+        _compare(cfg, dev.results(), ref, 1e-5)
+    dev.close()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("zero_peers", [False, True])
+def test_bf16_small_stacks(name, zero_peers):
+    cfg = SMALL[name]
+    inp = gen.make_inputs(cfg, zero_peers=zero_peers)
+    ref = oschedule.run_step(inp, "serial_fine")
+    dev = DeviceShard(inp)
+    dev.step("overlap_fine")
+    _compare(cfg, dev.results(), ref, 2e-2)
+    dev.close()
+
+
+@pytest.mark.parametrize("name", ["pair_d64_ragged", "stack4_d64"])
+def test_schedules_bit_identical(name):
+    cfg = SMALL[name]
+    inp = gen.make_inputs(cfg)
+    dev = DeviceShard(inp)
+    dev.step("serial_fine")
+    base = dev.results()
+    for mode in MODES:
+        for graph in (False, True):
+            for _ in range(2):  # graph: first call captures, second replays
+                dev.step(mode, use_graph=graph)
+                _bitwise_equal(dev.results(), base)
+    dev.close()
+
+
+def test_layer_entry_points_match_schedule_step():
+    cfg = SMALL["stack4_d64"]
+    inp = gen.make_inputs(cfg)
+    dev = DeviceShard(inp)
+    dev.step("serial_fine")
+    base = dev.results()
+    L = cfg.n_layers
+    for l in range(L):
+        for sb in (0, 1):
+            dev.ctx.layer_fwd(l, sb)
+    for l in reversed(range(L)):
+        for sb in (0, 1):
+            dev.ctx.layer_bwd_recompute(l, sb)
+    dev.ctx.sync()
+    _bitwise_equal(dev.results(), base)
+    dev.close()
