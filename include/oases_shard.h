@@ -205,12 +205,26 @@ int oases_profile_end(oases_ctx *c, double *total_ms, int32_t *launches);
 int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int64_t peer_stride,
                           int32_t n_peers, void *out, int64_t n, void *stream);
 
-/* C[M,N] = A[M,K] B[N,K]^T (+ bias[N]), optional exact GeLU: act = 0 none,
- * 1 gelu (writes gelu(acc+bias) to c and, if pre != NULL, acc+bias to pre).
- * Storage-type operands; K, N multiples of 8; lda/ldb/ldc in elements. */
-int oases_gemm_fwd(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *a, int32_t lda,
-                   const void *b, int32_t ldb, const void *bias, int32_t act, void *c,
-                   int32_t ldc, void *pre, void *stream);
+/* General GEMM of the path: C[M,N] = sum_k A(m,k) B(k,n), float32 accumulation.
+ *   a_layout 0: A stored [M][lda] (k contiguous);  1: A stored [K][lda] (m contiguous)
+ *   b_layout 0: B stored [N][ldb] (k contiguous);  1: B stored [K][ldb] (n contiguous)
+ *   epilogue 0: C = acc;  1: C = acc + bias[n];  2: C = gelu(acc + bias[n]) and, if pre
+ *            != NULL, pre = acc + bias[n];  3: C = acc * gelu'(aux[m][n]);
+ *            4: C (float32) = acc, plus the old C when beta != 0.
+ * Supported: layouts (0,0) with epilogues 0-2 (forward / recompute), (0,1) with
+ * 0 and 3 (data gradient), (1,1) with 4 (weight gradient).  Storage-type
+ * operands; the contiguous dimension of every operand and N are multiples of
+ * 8; leading dimensions in elements, multiples of 8.  pre and C (epilogues
+ * 0-3) use ldc; aux uses ld_aux. */
+int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilogue, int32_t m,
+               int32_t n, int32_t k, const void *a, int32_t lda, const void *b, int32_t ldb,
+               void *c, int32_t ldc, const void *bias, void *pre, const void *aux, int32_t ld_aux,
+               int32_t beta, void *stream);
+
+/* Tile configuration of the bf16 GEMMs for this process: 0 = automatic (the
+ * default), 1..9 force one of the compiled tile shapes (tuning sweeps).
+ * Returns OASES_E_ARG for other values. */
+int oases_gemm_tile_variant(int32_t variant);
 
 /* Causal attention forward over [nb*s, 3a] QKV -> O [nb*s, a] and log-sum-exp
  * lse [nb, n_h, s] (float32, natural log).  bf16 only; d in {64, 128}. */

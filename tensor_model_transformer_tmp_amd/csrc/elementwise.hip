@@ -58,44 +58,71 @@ __global__ void __launch_bounds__(SUM_NT)
 }
 
 // ---------------------------------------------------------------------------
-// Column sums, two passes with a fixed order (no atomics):
-//   pass 1: partial[chunk][c] = sum of rows [chunk*64, chunk*64+64) of column c
-//   pass 2: db[c] = (beta ? db[c] : 0) + sum over chunks in increasing order
+// Column sums, two passes with a fixed summation order (no atomics), so the
+// bias gradient is bit-reproducible:
+//   pass 1: partial[chunk][c] = sum of rows [64 chunk, 64 chunk + 64) of column
+//           c.  A workgroup covers 256 columns x 64 rows: 8 row lanes each add
+//           8 rows (16-byte loads of 8 columns), then the 8 lane sums are
+//           added in lane order through LDS.
+//   pass 2: db[c] = (beta ? db[c] : 0) + sum over chunks in increasing order,
+//           8 chunk lanes per column, combined in lane order through LDS.
 // ---------------------------------------------------------------------------
 constexpr int CS_ROWS = 64;
 
 template <bool BF16>
 __global__ void __launch_bounds__(256)
     colsum_pass1(const void *__restrict__ x, int rows, int cols, int ldx, float *__restrict__ partial) {
-  const int c8 = (blockIdx.x * 256 + threadIdx.x) * 8;  // 8 consecutive columns per thread
-  const int chunk = blockIdx.y;
-  if (c8 >= cols) return;
+  __shared__ float sm[8][257];
+  const int cg = threadIdx.x & 31, rl = threadIdx.x >> 5;
+  const int c8 = blockIdx.x * 256 + cg * 8;
+  const int r0 = blockIdx.y * CS_ROWS;
   float acc[8] = {};
-  const int r1 = min(rows, (chunk + 1) * CS_ROWS);
-  for (int r = chunk * CS_ROWS; r < r1; ++r) {
-    if constexpr (BF16) {
-      const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(x) + (int64_t)r * ldx + c8);
-      acc[0] += lo_f32(a.x); acc[1] += hi_f32(a.x); acc[2] += lo_f32(a.y); acc[3] += hi_f32(a.y);
-      acc[4] += lo_f32(a.z); acc[5] += hi_f32(a.z); acc[6] += lo_f32(a.w); acc[7] += hi_f32(a.w);
-    } else {
-      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)r * ldx + c8);
-      const float4 a = p[0], b = p[1];
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  if (c8 < cols) {
+#pragma unroll
+    for (int i = 0; i < CS_ROWS / 8; ++i) {
+      const int r = r0 + rl + 8 * i;
+      if (r >= rows) break;
+      if constexpr (BF16) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(x) + (int64_t)r * ldx + c8);
+        acc[0] += lo_f32(a.x); acc[1] += hi_f32(a.x); acc[2] += lo_f32(a.y); acc[3] += hi_f32(a.y);
+        acc[4] += lo_f32(a.z); acc[5] += hi_f32(a.z); acc[6] += lo_f32(a.w); acc[7] += hi_f32(a.w);
+      } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)r * ldx + c8);
+        const float4 a = p[0], b = p[1];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      }
     }
   }
-  float4 *o = reinterpret_cast<float4 *>(partial + (int64_t)chunk * cols + c8);
-  o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm[rl][cg * 8 + e] = acc[e];
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < cols) {
+    float t = sm[0][threadIdx.x];
+#pragma unroll
+    for (int l = 1; l < 8; ++l) t += sm[l][threadIdx.x];
+    partial[(int64_t)blockIdx.y * cols + c] = t;
+  }
 }
 
 __global__ void __launch_bounds__(256)
     colsum_pass2(const float *__restrict__ partial, int nchunks, int cols, float *__restrict__ db, int beta) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  float acc = beta ? db[c] : 0.f;
-  for (int ch = 0; ch < nchunks; ++ch) acc += partial[(int64_t)ch * cols + c];
-  db[c] = acc;
+  __shared__ float sm[8][33];
+  const int cl = threadIdx.x & 31, ch = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + cl;
+  float t = 0.f;
+  if (c < cols)
+    for (int k = ch; k < nchunks; k += 8) t += partial[(int64_t)k * cols + c];
+  sm[ch][cl] = t;
+  __syncthreads();
+  if (threadIdx.x < 32 && c < cols) {
+    float r = beta ? db[c] : 0.f;
+    float u = sm[0][cl];
+#pragma unroll
+    for (int l = 1; l < 8; ++l) u += sm[l][cl];
+    db[c] = r + u;
+  }
 }
 
 }  // namespace
@@ -127,14 +154,14 @@ hipError_t colsum(bool bf16, const void *x, int rows, int cols, int ldx, float *
   if (cols <= 0) return hipSuccess;
   const int nchunks = (rows + CS_ROWS - 1) / CS_ROWS;
   if (nchunks > 0) {
-    dim3 g1((cols / 8 + 255) / 256, nchunks);
+    dim3 g1((cols + 255) / 256, nchunks);
     if (bf16)
       hipLaunchKernelGGL(colsum_pass1<true>, g1, dim3(256), 0, s, x, rows, cols, ldx, partial);
     else
       hipLaunchKernelGGL(colsum_pass1<false>, g1, dim3(256), 0, s, x, rows, cols, ldx, partial);
   }
-  hipLaunchKernelGGL(colsum_pass2, dim3((cols + 255) / 256), dim3(256), 0, s, partial, nchunks,
-                     cols, db, beta);
+  hipLaunchKernelGGL(colsum_pass2, dim3((cols + 31) / 32), dim3(256), 0, s, partial, nchunks, cols, db,
+                     beta);
   return hipGetLastError();
 }
 

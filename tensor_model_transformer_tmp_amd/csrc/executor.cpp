@@ -682,24 +682,46 @@ int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int
   return e == hipSuccess ? OASES_OK : OASES_E_HIP;
 }
 
-int oases_gemm_fwd(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *a, int32_t lda,
-                   const void *b, int32_t ldb, const void *bias, int32_t act, void *c_, int32_t ldc,
-                   void *pre, void *stream) {
+int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilogue, int32_t m,
+               int32_t n, int32_t k, const void *a, int32_t lda, const void *b, int32_t ldb,
+               void *c_, int32_t ldc, const void *bias, void *pre, const void *aux, int32_t ld_aux,
+               int32_t beta, void *stream) {
   if (dtype != OASES_F32 && dtype != OASES_BF16) return OASES_E_ARG;
-  if (m < 0 || n < 0 || k < 0 || n % 8 || k % 8 || (act != 0 && act != 1)) return OASES_E_ARG;
+  if ((a_layout != 0 && a_layout != 1) || (b_layout != 0 && b_layout != 1)) return OASES_E_ARG;
+  const bool fwd = a_layout == 0 && b_layout == 0, dx = a_layout == 0 && b_layout == 1,
+             dw = a_layout == 1 && b_layout == 1;
+  if (!((fwd && epilogue >= 0 && epilogue <= 2) || (dx && (epilogue == 0 || epilogue == 3)) ||
+        (dw && epilogue == 4)))
+    return OASES_E_UNSUPPORTED;
+  if (m < 0 || n < 0 || k < 0 || n % 8) return OASES_E_ARG;
   if (m == 0 || n == 0) return OASES_OK;
-  if (!a || !b || !c_ || (act == 1 && !bias)) return OASES_E_ARG;
-  if (lda < k || ldb < k || ldc < n || lda % 8 || ldb % 8 || ldc % 8) return OASES_E_ARG;
+  if (!a || !b || !c_) return OASES_E_ARG;
+  if ((epilogue == 1 || epilogue == 2) && !bias) return OASES_E_ARG;
+  if (epilogue == 3 && (!aux || ld_aux < n || ld_aux % 8)) return OASES_E_ARG;
+  // contiguous dimension of each operand: A: k (layout 0) or m (1); B: k (0) or n (1)
+  const int a_cont = a_layout == 0 ? k : m, a_rows = a_layout == 0 ? m : k;
+  const int b_cont = b_layout == 0 ? k : n, b_rows = b_layout == 0 ? n : k;
+  (void)a_rows; (void)b_rows;
+  if (a_cont % 8 || b_cont % 8 || lda < a_cont || ldb < b_cont || ldc < n || lda % 8 || ldb % 8 ||
+      ldc % 8)
+    return OASES_E_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c_) || (pre && !aligned16(pre)) ||
-      (bias && ((uintptr_t)bias & 7)))
+      (aux && !aligned16(aux)) || (bias && ((uintptr_t)bias & 7)))
     return OASES_E_ALIGN;
   GemmArgs g{};
   g.M = m; g.N = n; g.K = k; g.A = a; g.lda = lda; g.B = b; g.ldb = ldb; g.C = c_; g.ldc = ldc;
-  g.bias = bias; g.pre = pre; g.ld_pre = ldc;
-  const Epi epi = act == 1 ? EPI_BIAS_GELU : (bias ? EPI_BIAS : EPI_STORE);
-  const hipError_t e = dtype == OASES_BF16 ? gemm_bf16(KC, KC, epi, g, static_cast<hipStream_t>(stream))
-                                           : gemm_f32(KC, KC, epi, g, static_cast<hipStream_t>(stream));
+  g.bias = bias; g.pre = pre; g.ld_pre = ldc; g.aux = aux; g.ld_aux = ld_aux; g.beta = beta;
+  const oases::Layout la = a_layout ? MC : KC, lb = b_layout ? MC : KC;
+  const Epi epi = static_cast<Epi>(epilogue);
+  const hipError_t e = dtype == OASES_BF16 ? gemm_bf16(la, lb, epi, g, static_cast<hipStream_t>(stream))
+                                           : gemm_f32(la, lb, epi, g, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? OASES_OK : OASES_E_HIP;
+}
+
+int oases_gemm_tile_variant(int32_t variant) {
+  if (variant < 0 || variant > 9) return OASES_E_ARG;
+  gemm_bf16_set_variant(variant);
+  return OASES_OK;
 }
 
 int oases_attention_fwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t causal, const void *qkv,

@@ -1,5 +1,5 @@
 // bf16 GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), float32
-// accumulation, LDS double-buffered 64-deep k tiles.
+// accumulation, multi-stage LDS ring with 64-deep k tiles.
 //
 // Used for the column-parallel and row-parallel GEMMs of a TMP shard and for
 // their data and weight gradients:
@@ -7,127 +7,268 @@
 //   data gradient         dX[T, K] = dC[T, N] W[N, K]         (A KC, B MC)
 //   weight gradient       dW[N, K] = dC[T, N]^T X[T, K]       (A MC, B MC)
 //
-// Tiling: a workgroup computes a BM x BN tile of C with WGM x WGN waves.
-// Every operand tile is staged in LDS as [rows][64 + 8] bf16 with k
-// contiguous, so each MFMA fragment is one 16-byte LDS read.  Operands whose
-// contiguous dimension is not k (MC) are transposed in registers (8x8 bf16
-// blocks) on their way into LDS.  The MFMA computes the transposed tile
-// C^T = B^T A^T, so a lane owns one row m of C and runs of four consecutive
-// columns n, which the epilogue writes as 8- or 16-byte vectors.
+// Tiling: a workgroup of 4 waves (2 x 2) computes a BM x BN tile of C.  Each
+// operand tile is held in LDS as [rows][64] bf16, k contiguous, with the
+// 16-byte chunks of row r XOR-swizzled by ((r ^ (r >> 3)) & 7) so that the
+// 16-byte fragment reads of 16 consecutive rows hit distinct banks of the
+// 64-bank LDS (measured: no bank-conflict cycles).
+//   * k-contiguous operands (KC) with K a multiple of 64 are copied HBM -> LDS
+//     by the gfx950 LDS DMA (global_load_lds_dwordx4), STAGES-1 tiles ahead,
+//     without passing through registers.
+//   * other operands go through registers: m/n-contiguous ones (MC) are read
+//     as 8x8 bf16 blocks and transposed in registers on their way into LDS.
+// The MFMA computes the transposed tile C^T = B^T A^T, so a lane owns one row
+// m of C and runs of four consecutive columns n, which the epilogue writes as
+// 8- or 16-byte vectors.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace oases {
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // LDS row pitch in bf16 (144 bytes: conflict-free 16-byte reads)
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
-template <int ROWS, int NT, Layout LAY>
-struct TileLoader {
-  // KC: ROWS*8 16-byte chunks; MC: ROWS 8x8 blocks (8 loads each)
-  static constexpr int ITEMS = (LAY == KC) ? (ROWS * 8 + NT - 1) / NT : (ROWS + NT - 1) / NT;
-  static constexpr int REGS = (LAY == KC) ? ITEMS : ITEMS * 8;
-  uint4 r[REGS];
+constexpr int BK = 64;          // k tile (elements)
+constexpr int ROWB = BK * 2;    // LDS bytes per tile row (unpadded, swizzled)
 
-  // rows_total: extent of the row dimension of the tile's matrix (M or N)
-  __device__ __forceinline__ void load(const bf16_t *__restrict__ p, int ld, int row0,
-                                       int rows_total, int k0, int K, int tid) {
-    if constexpr (LAY == KC) {
+
+// element offset of (row, 16-byte chunk) in a swizzled [rows][64] tile.
+// SW 0: chunk ^ (row & 7) -- distinct banks for 8 consecutive rows (32 banks);
+// SW 1: chunk ^ ((row ^ (row >> 3)) & 7) -- also distinct across 16 rows (64 banks).
+template <int SW>
+__device__ __forceinline__ int swz_key(int row) { return SW ? ((row ^ (row >> 3)) & 7) : (row & 7); }
+template <int SW>
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key<SW>(row)) << 3); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS only.  The step's global-memory traffic
+// needs no ordering across it (DMA completion is awaited explicitly with
+// vmcnt), so a full __syncthreads would needlessly drain every outstanding
+// load before each k tile.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One LDS-DMA instruction: every lane copies 16 bytes from its global address;
+// the wave's 64 x 16 bytes land contiguously at the LDS address `dst` (M0).
+// Issued as inline asm so that the compiler's memory model does not treat the
+// DMA as a pending LDS store: a fenced barrier would otherwise drain all
+// outstanding DMA before every k tile.  Completion is awaited explicitly with
+// wait_vmcnt() before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const bf16_t *src, const bf16_t *dst) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)dst;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+               : "m0", "memory");
+}
+
+// ---- operand loaders ------------------------------------------------------
+//
+// Every operand tile goes HBM -> LDS by DMA, one 1-KB wave instruction at a
+// time.  Lanes whose source lies outside the matrix (row past the end, or k
+// past K) read a zero page instead, so partial tiles and k tails are exact.
+
+__device__ __attribute__((aligned(64))) bf16_t g_zero_page[32];  // zero-initialised
+
+// KC tile: [ROWS][64] (k contiguous), chunk c of row r stored at c ^ swz_key(r).
+template <int ROWS, int NW>
+struct KcTile {
+  static constexpr int PER_WAVE = ROWS / 8 / NW;  // DMA instructions per wave per stage
+  __device__ __forceinline__ static void issue(const bf16_t *p, int ld, int row0, int rows_total,
+                                               int k0, int K, bf16_t *tile, int wave, int lane) {
 #pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        const int c = tid + i * NT;
-        const int row = c >> 3, kc = c & 7;
-        const int gr = row0 + row, gk = k0 + kc * 8;
-        const bool ok = (c < ROWS * 8) && gr < rows_total && gk < K;
-        r[i] = ok ? *reinterpret_cast<const uint4 *>(p + (int64_t)gr * ld + gk)
-                  : make_uint4(0, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        const int b = tid + i * NT;
-        const int kb = b & 7, rb = b >> 3;
-        const int gc = row0 + rb * 8;
-        const bool okc = (b < ROWS) && gc < rows_total;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int gk = k0 + kb * 8 + q;
-          r[i * 8 + q] = (okc && gk < K)
-                             ? *reinterpret_cast<const uint4 *>(p + (int64_t)gk * ld + gc)
-                             : make_uint4(0, 0, 0, 0);
-        }
-      }
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = j * NW + wave;               // 8-row block of the tile
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz_key<1>(r);    // global chunk landing at LDS chunk lane & 7
+      const bool ok = row0 + r < rows_total && k0 + c * 8 < K;
+      dma16(ok ? p + (int64_t)(row0 + r) * ld + k0 + c * 8 : g_zero_page, tile + blk * 8 * BK);
     }
   }
-
-  __device__ __forceinline__ void store(bf16_t *__restrict__ s, int tid) {
-    if constexpr (LAY == KC) {
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        const int c = tid + i * NT;
-        if (c < ROWS * 8) {
-          const int row = c >> 3, kc = c & 7;
-          *reinterpret_cast<uint4 *>(s + row * LDK + kc * 8) = r[i];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        const int b = tid + i * NT;
-        if (b < ROWS) {
-          const int kb = b & 7, rb = b >> 3;
-          uint4 blk[8], t[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) blk[q] = r[i * 8 + q];
-          transpose8x8_bf16(blk, t);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<uint4 *>(s + (rb * 8 + j) * LDK + kb * 8) = t[j];
-        }
-      }
-    }
+  // MFMA fragment: 8 consecutive k (half hl of substep ks) of tile row `row`
+  __device__ __forceinline__ static bf16x8 frag(const bf16_t *tile, int row, int ks, int hl) {
+    return *reinterpret_cast<const bf16x8 *>(tile + swz<1>(row, ks * 2 + hl));
   }
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// MC tile: [64 k][ROWS] (row index contiguous), 16-byte chunk c of k-row k
+// stored at c ^ 4 (k & 3).  Fragments are read with the gfx950 transposing
+// LDS read: in each 16-lane group, source lane s addresses k-row k0 + s/4 at
+// columns n0 + 4 (s % 4); lane i of the group then receives k0..k0+3 of column
+// n0 + i.  Two such reads give the 8 consecutive k of a KC fragment, so both
+// tile kinds feed the same MFMA.  The swizzle spreads the 4 k-rows of a read
+// over the four 64-byte quarters of the 256-byte bank space.
+template <int ROWS, int NW>
+struct McTile {
+  static constexpr int PER_WAVE = ROWS / 8 / NW;
+  static constexpr int ROW_BYTES = ROWS * 2;
+  __device__ __forceinline__ static void issue(const bf16_t *p, int ld, int col0, int cols_total,
+                                               int k0, int K, bf16_t *tile, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = j * NW + wave;               // 1-KB block of the tile
+      const int byte = blk * 1024 + lane * 16;
+      const int kr = byte / ROW_BYTES, cp = (byte % ROW_BYTES) >> 4;
+      const int c = cp ^ ((kr & 3) << 2);
+      const bool ok = k0 + kr < K && col0 + c * 8 < cols_total;
+      dma16(ok ? p + (int64_t)(k0 + kr) * ld + col0 + c * 8 : g_zero_page, tile + blk * 512);
+    }
+  }
+  __device__ __forceinline__ static bf16x8 frag(const bf16_t *tile, int row, int ks, int hl) {
+    // `row` is this lane's column of the operand (its m or n); the group's base is row - (lane & 15)
+    const int lane = threadIdx.x & 63, s = lane & 15;
+    const int n = (row - s) + 4 * (s & 3);
+    v4i16 v[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int k = ks * 16 + hl * 8 + r * 4 + (s >> 2);
+      const bf16_t *a = tile + k * ROWS + ((((n >> 3) ^ ((k & 3) << 2))) << 3) + (n & 7);
+      v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(lds_void_t *)a);
+    }
+    const uint2 lo = __builtin_bit_cast(uint2, v[0]), hi = __builtin_bit_cast(uint2, v[1]);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+};
+
+template <int ROWS, int NW, Layout L>
+using Tile = typename std::conditional<L == KC, KcTile<ROWS, NW>, McTile<ROWS, NW>>::type;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int BM, int BN, int WGM, int WGN, Layout LA, Layout LB, int EPI>
-__global__ void __launch_bounds__(WGM *WGN * 64)
-    gemm_bf16_kernel(GemmArgs g) {
-  constexpr int NT = WGM * WGN * 64;
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  static_assert(TM >= 1 && TN >= 1, "wave tile must be a multiple of 32");
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDK];
+// ---- epilogue ---------------------------------------------------------------
+//
+// A lane owns, for each of its TM row groups i, one row m and TN*4 runs of four
+// consecutive columns.  Every global load an epilogue needs for row group i
+// (bias, the GeLU input, the old float32 C) is issued before any of its math
+// or stores, so the group waits for memory once instead of once per run.
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+template <int EPI, int TN>
+__device__ __forceinline__ void epilogue_row(const GemmArgs &g, int m, const int (&ncol)[TN][4],
+                                             float (&v)[TN][4][4]) {
+  constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_GELU;
+  uint2 in[TN][4];  // bias or aux (bf16 x 4)
+  float4 old[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int n = ncol[j][jj];
+      if (n >= g.N) continue;
+      if constexpr (BIAS) in[j][jj] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(g.bias) + n);
+      if constexpr (EPI == EPI_GELU_BWD)
+        in[j][jj] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(g.aux) + (int64_t)m * g.ld_aux + n);
+      if constexpr (EPI == EPI_F32)
+        if (g.beta) old[j][jj] = *reinterpret_cast<const float4 *>(static_cast<float *>(g.C) + (int64_t)m * g.ldc + n);
+    }
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int n = ncol[j][jj];
+      if (n >= g.N) continue;
+      float *x = v[j][jj];
+      if constexpr (EPI == EPI_F32) {
+        float4 o = make_float4(x[0], x[1], x[2], x[3]);
+        if (g.beta) { o.x += old[j][jj].x; o.y += old[j][jj].y; o.z += old[j][jj].z; o.w += old[j][jj].w; }
+        *reinterpret_cast<float4 *>(static_cast<float *>(g.C) + (int64_t)m * g.ldc + n) = o;
+        continue;
+      }
+      if constexpr (BIAS) {
+        x[0] += lo_f32(in[j][jj].x); x[1] += hi_f32(in[j][jj].x);
+        x[2] += lo_f32(in[j][jj].y); x[3] += hi_f32(in[j][jj].y);
+      }
+      if constexpr (EPI == EPI_BIAS_GELU) {
+        if (g.pre)
+          *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(g.pre) + (int64_t)m * g.ld_pre + n) =
+              make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) x[ii] = gelu_f(x[ii]);
+      }
+      if constexpr (EPI == EPI_GELU_BWD) {
+        x[0] *= gelu_grad_f(lo_f32(in[j][jj].x)); x[1] *= gelu_grad_f(hi_f32(in[j][jj].x));
+        x[2] *= gelu_grad_f(lo_f32(in[j][jj].y)); x[3] *= gelu_grad_f(hi_f32(in[j][jj].y));
+      }
+      *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(g.C) + (int64_t)m * g.ldc + n) =
+          make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+    }
+}
+
+// ---- kernel -----------------------------------------------------------------
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
+  static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM >= 1 && TN >= 1 && (BM / 8) % NW == 0 && (BN / 8) % NW == 0, "tile shape");
+  using TA = Tile<BM, NW, LA>;
+  using TB = Tile<BN, NW, LB>;
+  constexpr int DL = TA::PER_WAVE + TB::PER_WAVE;  // DMA instructions per wave per stage
+  // One LDS variable per stage and operand, selected with compile-time slot
+  // indices, so the compiler sees that the fragment reads of one stage and
+  // the DMA into another do not alias.
+  __shared__ __attribute__((aligned(1024))) bf16_t sA0[BM * BK], sA1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB0[BN * BK], sB1[BN * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA2[STAGES > 2 ? BM * BK : 8], sB2[STAGES > 2 ? BN * BK : 8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;  // hl: which 32-lane half
   const int wm = wave % WGM, wn = wave / WGM;
 
-  // tile order: consecutive workgroups of one XCD (ids i, i+8, ...) take
-  // neighbouring tiles, grouped 8 m-tiles at a time along n for L2 reuse
+  // tile order: workgroups i, i+8, ... run on one XCD; give them neighbouring
+  // tiles, grouped 8 m-tiles at a time along n, so an XCD's L2 sees reuse
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
   if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
   constexpr int GROUP = 8;
   const int group_span = GROUP * tiles_n;
-  const int grp = bid / group_span;
-  const int first_m = grp * GROUP;
+  const int first_m = (bid / group_span) * GROUP;
   const int gsize = min(tiles_m - first_m, GROUP);
   const int tm = first_m + (bid % group_span) % gsize;
   const int tn = (bid % group_span) / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const bf16_t *__restrict__ A = static_cast<const bf16_t *>(g.A);
-  const bf16_t *__restrict__ B = static_cast<const bf16_t *>(g.B);
-  TileLoader<BM, NT, LA> la;
-  TileLoader<BN, NT, LB> lb;
+  const bf16_t *A = static_cast<const bf16_t *>(g.A);
+  const bf16_t *B = static_cast<const bf16_t *>(g.B);
+  const int nk = (g.K + BK - 1) / BK;
+
+  auto slotA = [&](auto I) -> bf16_t * {
+    if constexpr (decltype(I)::value == 0) return sA0;
+    else if constexpr (decltype(I)::value == 1) return sA1;
+    else return sA2;
+  };
+  auto slotB = [&](auto I) -> bf16_t * {
+    if constexpr (decltype(I)::value == 0) return sB0;
+    else if constexpr (decltype(I)::value == 1) return sB1;
+    else return sB2;
+  };
+  auto issue = [&](auto I, int stage) {
+    TA::issue(A, g.lda, m0, g.M, stage * BK, g.K, slotA(I), wave, lane);
+    TB::issue(B, g.ldb, n0, g.N, stage * BK, g.K, slotB(I), wave, lane);
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
 
   f32x16 acc[TN][TM];
 #pragma unroll
@@ -137,112 +278,133 @@ __global__ void __launch_bounds__(WGM *WGN * 64)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
-  const int nk = (g.K + BK - 1) / BK;
-  la.load(A, g.lda, m0, g.M, 0, g.K, tid);
-  lb.load(B, g.ldb, n0, g.N, 0, g.K, tid);
-  la.store(sA[0], tid);
-  lb.store(sB[0], tid);
-  __syncthreads();
+  // prologue: stages 0 .. STAGES-2 in flight
+  issue(C0{}, 0);
+  if constexpr (STAGES == 3)
+    if (nk > 1) issue(C1{}, 1);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(A, g.lda, m0, g.M, (kt + 1) * BK, g.K, tid);
-      lb.load(B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, tid);
-    }
-    const bf16_t *a_s = sA[buf] + (wm * WTM + l32) * LDK + hl * 8;
-    const bf16_t *b_s = sB[buf] + (wn * WTN + l32) * LDK + hl * 8;
+  // one k tile in LDS slot I (static); stage kt+STAGES-1 goes to slot I+STAGES-1
+  auto step = [&](auto I, int kt) {
+    using AHEAD = std::integral_constant<int, (decltype(I)::value + STAGES - 1) % STAGES>;
+    // this stage's DMA is done once at most the later stage's DMA is outstanding
+    if (STAGES == 3 && kt + 1 < nk) wait_vmcnt<DL>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (kt + STAGES - 1 < nk) issue(AHEAD{}, kt + STAGES - 1);
+
+    const bf16_t *a_s = slotA(I);
+    const bf16_t *b_s = slotB(I);
+    // fragments double-buffered in registers: the LDS reads of k-substep
+    // ks+1 are issued while the MFMAs of ks run
+    bf16x8 xa[2][TM], wb[2][TN];
+    auto read_frags = [&](int ks, int buf) {
+#pragma unroll
+      for (int i2 = 0; i2 < TM; ++i2) xa[buf][i2] = TA::frag(a_s, wm * WTM + i2 * 32 + l32, ks, hl);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) wb[buf][j] = TB::frag(b_s, wn * WTN + j * 32 + l32, ks, hl);
+    };
+    read_frags(0, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 xa[TM], wb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        xa[i] = *reinterpret_cast<const bf16x8 *>(a_s + i * 32 * LDK + ks * 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        wb[j] = *reinterpret_cast<const bf16x8 *>(b_s + j * 32 * LDK + ks * 16);
+      if (ks + 1 < BK / 16) read_frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) acc[j][i] = mfma32(wb[j], xa[i], acc[j][i]);
+        for (int i2 = 0; i2 < TM; ++i2) acc[j][i2] = mfma32(wb[ks & 1][j], xa[ks & 1][i2], acc[j][i2]);
     }
-    if (more) {
-      la.store(sA[buf ^ 1], tid);
-      lb.store(sB[buf ^ 1], tid);
+    // schedule: fragment reads of substep 0, then each MFMA of substep ks
+    // followed by one LDS read of substep ks+1
+    constexpr int RD = TM * (LA == KC ? 1 : 2) + TN * (LB == KC ? 1 : 2), MF = TM * TN;
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+#pragma unroll
+      for (int t = 0; t < MF; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks + 1 < BK / 16) {
+          constexpr int PER = (RD + MF - 1) / MF;  // reads to place after each MFMA
+#pragma unroll
+          for (int q = 0; q < PER; ++q)
+            if (t * PER + q < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
     }
-    __syncthreads();
+  };
+
+  // full groups of STAGES k tiles (slots 0..STAGES-1 in order), then the tail
+  int kt = 0;
+  for (; kt + STAGES <= nk; kt += STAGES) {
+    step(C0{}, kt);
+    step(C1{}, kt + 1);
+    if constexpr (STAGES == 3) step(C2{}, kt + 2);
   }
+  if (kt < nk) step(C0{}, kt);
+  if constexpr (STAGES == 3)
+    if (kt + 1 < nk) step(C1{}, kt + 1);
 
   // epilogue: acc[j][i][jj*4 + ii] is C[m][n] with
   //   m = m0 + wm*WTM + i*32 + l32,  n = n0 + wn*WTN + j*32 + jj*8 + hl*4 + ii
+  int ncol[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) ncol[j][jj] = n0 + wn * WTN + j * 32 + jj * 8 + hl * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + wm * WTM + i * 32 + l32;
     if (m >= g.M) continue;
+    float v[TN][4][4];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int n = n0 + wn * WTN + j * 32 + jj * 8 + hl * 4;
-        if (n >= g.N) continue;
-        float v[4];
+      for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) v[ii] = acc[j][i][jj * 4 + ii];
-        if constexpr (EPI == EPI_F32) {
-          float *c = static_cast<float *>(g.C) + (int64_t)m * g.ldc + n;
-          float4 o = make_float4(v[0], v[1], v[2], v[3]);
-          if (g.beta) {
-            const float4 old = *reinterpret_cast<const float4 *>(c);
-            o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
-          }
-          *reinterpret_cast<float4 *>(c) = o;
-        } else {
-          if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
-            const uint2 bb = *reinterpret_cast<const uint2 *>(
-                static_cast<const bf16_t *>(g.bias) + n);
-            v[0] += lo_f32(bb.x); v[1] += hi_f32(bb.x);
-            v[2] += lo_f32(bb.y); v[3] += hi_f32(bb.y);
-          }
-          if constexpr (EPI == EPI_BIAS_GELU) {
-            if (g.pre) {
-              *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(g.pre) + (int64_t)m * g.ld_pre + n) =
-                  make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            }
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) v[ii] = gelu_f(v[ii]);
-          }
-          if constexpr (EPI == EPI_GELU_BWD) {
-            const uint2 uu = *reinterpret_cast<const uint2 *>(
-                static_cast<const bf16_t *>(g.aux) + (int64_t)m * g.ld_aux + n);
-            v[0] *= gelu_grad_f(lo_f32(uu.x)); v[1] *= gelu_grad_f(hi_f32(uu.x));
-            v[2] *= gelu_grad_f(lo_f32(uu.y)); v[3] *= gelu_grad_f(hi_f32(uu.y));
-          }
-          *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(g.C) + (int64_t)m * g.ldc + n) =
-              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
-      }
-    }
+        for (int ii = 0; ii < 4; ++ii) v[j][jj][ii] = acc[j][i][jj * 4 + ii];
+    epilogue_row<EPI, TN>(g, m, ncol, v);
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, Layout LA, Layout LB, int EPI>
+template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI>
 hipError_t launch(const GemmArgs &g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, LA, LB, EPI>), dim3(tiles),
-                     dim3(WGM * WGN * 64), 0, s, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, LA, LB, EPI>), dim3(tiles),
+                     dim3(64 * WGM * WGN), 0, s, g);
   return hipGetLastError();
 }
 
+int g_variant = 0;  // 0 = automatic tile choice; >0 forces one (tuning sweeps)
+
 template <Layout LA, Layout LB, int EPI>
 hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
-  // Large tiles when they alone fill the chip; otherwise 128x128 tiles.
-  const int64_t big_tiles = (int64_t)((g.M + 255) / 256) * ((g.N + 127) / 128);
-  if (big_tiles >= 256) return launch<256, 128, 2, 2, LA, LB, EPI>(g, s);
-  return launch<128, 128, 2, 2, LA, LB, EPI>(g, s);
+  int v = g_variant;
+  if (v == 0) {
+    // measured on MI355X over the workload shapes: 256x256 (8 waves) when it
+    // alone gives a tile per CU, 128x256 (8 waves) near that, otherwise
+    // 128x128 tiles (3 stages for long k loops, 2 stages / 2 per CU for short)
+    const int64_t t256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
+    const int64_t t128x256 = (int64_t)((g.M + 127) / 128) * ((g.N + 255) / 256);
+    if (t256 >= 256) v = 9;
+    else if (t128x256 >= 192) v = 8;
+    else if (g.K >= 2048) v = 2;
+    else v = 5;
+  }
+  switch (v) {
+    case 1: return launch<256, 128, 2, 2, 3, LA, LB, EPI>(g, s);
+    case 2: return launch<128, 128, 2, 2, 3, LA, LB, EPI>(g, s);
+    case 3: return launch<128, 256, 2, 2, 3, LA, LB, EPI>(g, s);
+    case 4: return launch<256, 256, 2, 2, 2, LA, LB, EPI>(g, s);
+    case 5: return launch<128, 128, 2, 2, 2, LA, LB, EPI>(g, s);
+    case 6: return launch<256, 128, 4, 2, 3, LA, LB, EPI>(g, s);
+    case 7: return launch<256, 256, 2, 4, 2, LA, LB, EPI>(g, s);
+    case 8: return launch<128, 256, 2, 4, 3, LA, LB, EPI>(g, s);
+    case 9: return launch<256, 256, 4, 2, 2, LA, LB, EPI>(g, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
+
+void gemm_bf16_set_variant(int v) { g_variant = v; }
 
 hipError_t gemm_bf16(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;

@@ -42,6 +42,7 @@ struct GemmArgs {
 // bf16 operands on MFMA; float32 operands on a SIMT kernel.
 hipError_t gemm_bf16(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream_t s);
 hipError_t gemm_f32(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream_t s);
+void gemm_bf16_set_variant(int v);
 
 // AllReduce point: out = own + sum_k peers[k] (float32 accumulation in order)
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,

@@ -27,7 +27,7 @@ KCLASS = {"gemm_fwd": 0, "gemm_dx": 1, "gemm_dw": 2, "attn_fwd": 3, "attn_bwd": 
 EXPORTED = ("oases_create", "oases_workspace_bytes", "oases_bind", "oases_set_streams",
             "layer_fwd", "layer_bwd_recompute", "schedule_step", "oases_schedule_ops",
             "oases_sync", "oases_last_error", "oases_destroy", "oases_profile_begin",
-            "oases_profile_end", "oases_allreduce_point", "oases_gemm_fwd",
+            "oases_profile_end", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
             "oases_attention_fwd")
 
 
@@ -78,7 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "oases_profile_begin": (ctypes.c_int, [P, I32, I32]),
         "oases_profile_end": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
         "oases_allreduce_point": (ctypes.c_int, [I32, P, P, I64, I32, P, I64, P]),
-        "oases_gemm_fwd": (ctypes.c_int, [I32, I32, I32, I32, P, I32, P, I32, P, I32, P, I32, P, P]),
+        "oases_gemm": (ctypes.c_int, [I32, I32, I32, I32, I32, I32, I32, P, I32, P, I32, P, I32, P, P,
+                                      P, I32, I32, P]),
+        "oases_gemm_tile_variant": (ctypes.c_int, [I32]),
         "oases_attention_fwd": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -233,12 +235,30 @@ def allreduce_point(dtype, own, peers, n_peers, out, stream=None):
                 "oases_allreduce_point")
 
 
+EPILOGUES = {"store": 0, "bias": 1, "gelu": 2, "gelu_bwd": 3, "f32": 4}
+
+
+def gemm(dtype, a, b, c, a_layout=0, b_layout=0, epilogue="store", m=None, n=None, k=None,
+         bias=None, pre=None, aux=None, beta=0, stream=None):
+    """C = A B with the operand layouts of the C ABI (0: k contiguous, 1: m/n contiguous)."""
+    if m is None:
+        m = a.shape[0] if a_layout == 0 else a.shape[1]
+        k = a.shape[1] if a_layout == 0 else a.shape[0]
+        n = b.shape[0] if b_layout == 0 else b.shape[1]
+    _check_free(lib().oases_gemm(dtype, a_layout, b_layout, EPILOGUES[epilogue], m, n, k, _ptr(a),
+                                 a.stride(0), _ptr(b), b.stride(0), _ptr(c), c.stride(0), _ptr(bias),
+                                 _ptr(pre), _ptr(aux), aux.stride(0) if aux is not None else 0,
+                                 int(beta), _stream_handle(stream)), "oases_gemm")
+
+
 def gemm_fwd(dtype, a, b, c, bias=None, gelu=False, pre=None, stream=None):
-    m, k = a.shape
-    n = b.shape[0]
-    _check_free(lib().oases_gemm_fwd(dtype, m, n, k, _ptr(a), a.stride(0), _ptr(b), b.stride(0),
-                                     _ptr(bias), int(gelu), _ptr(c), c.stride(0), _ptr(pre),
-                                     _stream_handle(stream)), "oases_gemm_fwd")
+    """C[M,N] = A[M,K] B[N,K]^T (+ bias) (GeLU)."""
+    epi = "gelu" if gelu else ("bias" if bias is not None else "store")
+    gemm(dtype, a, b, c, 0, 0, epi, bias=bias, pre=pre, stream=stream)
+
+
+def set_gemm_tile_variant(v: int):
+    _check_free(lib().oases_gemm_tile_variant(v), "oases_gemm_tile_variant")
 
 
 def attention_fwd(nb, s, nh, d, causal, qkv, o, lse, stream=None):

@@ -113,8 +113,19 @@ def test_single_kernel_entry_validation():
     assert L.oases_allreduce_point(1, 16, 32, 10, 1, 48, 12, None) == shard.E_ARG  # n % 8
     assert L.oases_allreduce_point(1, 17, 32, 16, 1, 48, 16, None) == shard.E_ALIGN
     assert L.oases_allreduce_point(1, 16, 32, 16, 1, 48, 0, None) == shard.OK  # empty
-    assert L.oases_gemm_fwd(1, 4, 12, 16, 16, 16, 32, 16, None, 0, 48, 16, None, None) == shard.E_ARG
-    assert L.oases_gemm_fwd(1, 0, 16, 16, 16, 16, 32, 16, None, 0, 48, 16, None, None) == shard.OK
+    # n % 8 != 0
+    assert L.oases_gemm(1, 0, 0, 0, 4, 12, 16, 16, 16, 32, 16, 48, 16, None, None, None, 0, 0,
+                        None) == shard.E_ARG
+    # unsupported layout / epilogue pair
+    assert L.oases_gemm(1, 1, 1, 0, 4, 16, 16, 16, 16, 32, 16, 48, 16, None, None, None, 0, 0,
+                        None) == shard.E_UNSUPPORTED
+    # bias epilogue without a bias
+    assert L.oases_gemm(1, 0, 0, 1, 4, 16, 16, 16, 16, 32, 16, 48, 16, None, None, None, 0, 0,
+                        None) == shard.E_ARG
+    # empty problem is a no-op
+    assert L.oases_gemm(1, 0, 0, 0, 0, 16, 16, 16, 16, 32, 16, 48, 16, None, None, None, 0, 0,
+                        None) == shard.OK
+    assert L.oases_gemm_tile_variant(10) == shard.E_ARG
     assert L.oases_attention_fwd(1, 8, 1, 96, 1, 16, 32, 48, None) == shard.E_ARG
 
 

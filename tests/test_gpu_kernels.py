@@ -102,3 +102,51 @@ def test_attention_fwd(d, nb, s, nh, causal):
     mx = sc.max(-1, keepdims=True)
     lse_ref = (mx + np.log(np.exp(sc - mx).sum(-1, keepdims=True)))[..., 0]
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-3)
+
+
+GEMM_SHAPES = [(200, 192, 128), (1000, 520, 576), (2048, 1024, 1024), (296, 136, 200), (64, 8, 64)]
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("kind", ["fwd", "dx", "dx_gelu", "dw"])
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_gemm_layouts_and_tiles(variant, kind, m, n, k):
+    """Every operand layout / epilogue of the step's GEMMs and every tile
+    configuration, against a float64 product of the same bf16 operands."""
+    rng = np.random.default_rng(m + 3 * n + 7 * k + variant)
+    dev = "cuda"
+    shard.set_gemm_tile_variant(variant)
+    try:
+        a_km = _bf16_bits(rng, (m, k))          # A(m, k), stored [M][K]
+        b_nk = _bf16_bits(rng, (n, k), 0.05)    # B(k, n) stored [N][K]
+        af = gen.bf16_bits_to_f64(a_km)
+        bf = gen.bf16_bits_to_f64(b_nk)
+        ref = af @ bf.T
+        if kind == "fwd":
+            c = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            shard.gemm(shard.BF16, to_device(a_km, gen.BF16, dev), to_device(b_nk, gen.BF16, dev), c,
+                       0, 0, "store")
+        elif kind.startswith("dx"):
+            b_kn = np.ascontiguousarray(b_nk.T)  # stored [K][N] (n contiguous)
+            c = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            aux = None
+            if kind == "dx_gelu":
+                u = _bf16_bits(rng, (m, n))
+                aux = to_device(u, gen.BF16, dev)
+                ref = ref * blocks.gelu_grad(gen.bf16_bits_to_f64(u))
+            shard.gemm(shard.BF16, to_device(a_km, gen.BF16, dev), to_device(b_kn, gen.BF16, dev), c,
+                       0, 1, "gelu_bwd" if aux is not None else "store", m=m, n=n, k=k, aux=aux)
+        else:
+            a_mk = np.ascontiguousarray(a_km.T)  # stored [K][M] (m contiguous)
+            b_kn = np.ascontiguousarray(b_nk.T)
+            old = rng.standard_normal((m, n)).astype(np.float32)
+            c = torch.from_numpy(old).to(dev)
+            shard.gemm(shard.BF16, to_device(a_mk, gen.BF16, dev), to_device(b_kn, gen.BF16, dev), c,
+                       1, 1, "f32", m=m, n=n, k=k, beta=1)
+            ref = ref + old
+        torch.cuda.synchronize()
+        got = c.cpu().numpy() if c.dtype == torch.float32 else gen.bf16_bits_to_f64(to_storage(c))
+        tol = 1e-5 if kind == "dw" else 8e-3
+        assert_close(got, ref, tol, f"{kind} {m}x{n}x{k} variant {variant}")
+    finally:
+        shard.set_gemm_tile_variant(0)
