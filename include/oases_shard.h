@@ -226,8 +226,16 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
  * Returns OASES_E_ARG for other values. */
 int oases_gemm_tile_variant(int32_t variant);
 
-/* Causal attention forward over [nb*s, 3a] QKV -> O [nb*s, a] and log-sum-exp
- * lse [nb, n_h, s] (float32, natural log).  bf16 only; d in {64, 128}. */
+/* Attention kernel layout for this process: 0 = automatic (the default),
+ * 1 = split (a workgroup owns 32 rows, its waves split the other dimension),
+ * 2 = query-parallel (a workgroup owns 128 rows sharing each staged block).
+ * For tests and tuning; OASES_E_ARG for other values. */
+int oases_attention_variant(int32_t variant);
+
+/* Causal (causal = 1) or full attention forward over QKV [nb*s, 3a]
+ * (columns [Q | K | V], each head-major) -> O [nb*s, a] and the per-row
+ * log-sum-exp lse [nb, n_h, s_pad] (float32, natural log, row stride
+ * s_pad = s rounded up to a multiple of 64).  bf16 only; d in {64, 128}. */
 int oases_attention_fwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t causal,
                         const void *qkv, void *o, float *lse, void *stream);
 

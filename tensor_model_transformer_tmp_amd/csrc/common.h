@@ -29,6 +29,57 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// 64 zero bytes in global memory: the source of DMA lanes whose element lies
+// outside a matrix, so partial tiles are filled with exact zeros.
+__device__ __forceinline__ const bf16_t *zero_page() {
+  static __device__ __attribute__((aligned(64))) bf16_t page[32];  // zero-initialised
+  return page;
+}
+
+// One LDS-DMA instruction (gfx950 global_load_lds_dwordx4): every lane copies
+// 16 bytes from its global address; the wave's 64 x 16 bytes land
+// contiguously at the LDS address `dst` (through M0).  Issued as inline asm
+// so that the compiler's memory model does not treat the DMA as a pending LDS
+// store (a fenced barrier would otherwise drain all outstanding DMA before
+// every tile); completion is awaited explicitly with wait_vmcnt().
+__device__ __forceinline__ void dma16(const bf16_t *src, const bf16_t *dst) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)dst;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+               : "m0", "memory");
+}
+
+// Chunk swizzle of a row-major bf16 tile read with ds_read_b64_tr_b16: a read
+// covers 4 consecutive rows x 64 bytes per 32 lanes.  16-byte chunk c of row
+// k is stored at c ^ mc_swz(k) so those rows land in distinct 64-byte
+// quarters of the 256-byte bank space: rows of >= 256 bytes use (k & 3),
+// 128-byte rows (two per bank window) use bit 1 of k.
+template <int ROW_ELEMS>
+__device__ __forceinline__ int mc_swz(int k) {
+  static_assert(ROW_ELEMS == 64 || ROW_ELEMS % 128 == 0, "row length");
+  return ROW_ELEMS == 64 ? (((k >> 1) & 1) << 2) : ((k & 3) << 2);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS only (global traffic needs no ordering
+// across it: DMA completion is awaited with wait_vmcnt before it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Transpose an 8x8 block of bf16 held as 8 rows of uint4 (row i = r[i], 8
 // elements each) into 8 columns: o[j] holds element j of r[0..7].
 __device__ __forceinline__ void transpose8x8_bf16(const uint4 (&r)[8], uint4 (&o)[8]) {
@@ -49,13 +100,41 @@ __device__ __forceinline__ void transpose8x8_bf16(const uint4 (&r)[8], uint4 (&o
   }
 }
 
-// exact GeLU and its derivative in float32: gelu(u) = u * Phi(u)
-__device__ __forceinline__ float gelu_f(float u) {
-  return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+// GeLU and its derivative in float32, gelu(u) = u * Phi(u) with the standard
+// normal CDF Phi(u) = (1 + erf(u / sqrt 2)) / 2.  erf is evaluated with the
+// rational-exponential approximation 7.1.26 of Abramowitz & Stegun (Handbook
+// of Mathematical Functions): for x >= 0,
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x),  |error| <= 1.5e-7,
+// which is below float32 resolution of Phi near 1 and far below bf16
+// resolution.  The tail Q = 1 - erf(x) is formed directly (no cancellation)
+// and its exp(-x^2) = exp(-u^2 / 2) is shared with the density in gelu'.
+struct PhiParts {
+  float phi_cdf;  // Phi(u)
+  float pdf;      // phi(u) = exp(-u^2/2) / sqrt(2 pi)
+};
+
+__device__ __forceinline__ PhiParts normal_cdf_pdf(float u) {
+  const float x = fabsf(u) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);  // exp(-x^2)
+  const float half_q = 0.5f * poly * e;                                  // (1 - erf(x)) / 2
+  PhiParts r;
+  r.phi_cdf = u >= 0.f ? 1.0f - half_q : half_q;
+  r.pdf = 0.39894228040143268f * e;
+  return r;
 }
+
+__device__ __forceinline__ float gelu_f(float u) { return u * normal_cdf_pdf(u).phi_cdf; }
+
 __device__ __forceinline__ float gelu_grad_f(float u) {
-  return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) +
-         u * 0.39894228040143268f * expf(-0.5f * u * u);
+  const PhiParts p = normal_cdf_pdf(u);
+  return fmaf(u, p.pdf, p.phi_cdf);
 }
 
 }  // namespace oases

@@ -72,7 +72,7 @@ WsLayout make_layout(const Dims &D, int mode) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t r = off; off = align_up(off + bytes); return r; };
   const size_t th = (size_t)D.T * D.h * D.esz;
-  const size_t lse_bytes = (size_t)D.nb * D.ns * D.s * sizeof(float);
+  const size_t lse_bytes = (size_t)D.nb * D.ns * attn_lse_stride(D.s) * sizeof(float);
   for (int sb = 0; sb < 2; ++sb) {
     o.P[sb] = take(th);
     o.dxo[sb] = take(th);
@@ -718,8 +718,14 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
   return e == hipSuccess ? OASES_OK : OASES_E_HIP;
 }
 
+int oases_attention_variant(int32_t variant) {
+  if (variant < 0 || variant > 2) return OASES_E_ARG;
+  attention_set_variant(variant);
+  return OASES_OK;
+}
+
 int oases_gemm_tile_variant(int32_t variant) {
-  if (variant < 0 || variant > 9) return OASES_E_ARG;
+  if (variant < 0 || variant > 11) return OASES_E_ARG;
   gemm_bf16_set_variant(variant);
   return OASES_OK;
 }

@@ -28,9 +28,6 @@
 namespace oases {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
 constexpr int BK = 64;          // k tile (elements)
 constexpr int ROWB = BK * 2;    // LDS bytes per tile row (unpadded, swizzled)
 
@@ -43,44 +40,11 @@ __device__ __forceinline__ int swz_key(int row) { return SW ? ((row ^ (row >> 3)
 template <int SW>
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key<SW>(row)) << 3); }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that orders LDS only.  The step's global-memory traffic
-// needs no ordering across it (DMA completion is awaited explicitly with
-// vmcnt), so a full __syncthreads would needlessly drain every outstanding
-// load before each k tile.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// One LDS-DMA instruction: every lane copies 16 bytes from its global address;
-// the wave's 64 x 16 bytes land contiguously at the LDS address `dst` (M0).
-// Issued as inline asm so that the compiler's memory model does not treat the
-// DMA as a pending LDS store: a fenced barrier would otherwise drain all
-// outstanding DMA before every k tile.  Completion is awaited explicitly with
-// wait_vmcnt() before the barrier that publishes the tile.
-__device__ __forceinline__ void dma16(const bf16_t *src, const bf16_t *dst) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)dst;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
-               : "m0", "memory");
-}
-
 // ---- operand loaders ------------------------------------------------------
 //
 // Every operand tile goes HBM -> LDS by DMA, one 1-KB wave instruction at a
 // time.  Lanes whose source lies outside the matrix (row past the end, or k
 // past K) read a zero page instead, so partial tiles and k tails are exact.
-
-__device__ __attribute__((aligned(64))) bf16_t g_zero_page[32];  // zero-initialised
 
 // KC tile: [ROWS][64] (k contiguous), chunk c of row r stored at c ^ swz_key(r).
 template <int ROWS, int NW>
@@ -94,7 +58,7 @@ struct KcTile {
       const int r = blk * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz_key<1>(r);    // global chunk landing at LDS chunk lane & 7
       const bool ok = row0 + r < rows_total && k0 + c * 8 < K;
-      dma16(ok ? p + (int64_t)(row0 + r) * ld + k0 + c * 8 : g_zero_page, tile + blk * 8 * BK);
+      dma16(ok ? p + (int64_t)(row0 + r) * ld + k0 + c * 8 : zero_page(), tile + blk * 8 * BK);
     }
   }
   // MFMA fragment: 8 consecutive k (half hl of substep ks) of tile row `row`
@@ -103,11 +67,8 @@ struct KcTile {
   }
 };
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
-
 // MC tile: [64 k][ROWS] (row index contiguous), 16-byte chunk c of k-row k
-// stored at c ^ 4 (k & 3).  Fragments are read with the gfx950 transposing
+// stored at c ^ mc_swz(k).  Fragments are read with the gfx950 transposing
 // LDS read: in each 16-lane group, source lane s addresses k-row k0 + s/4 at
 // columns n0 + 4 (s % 4); lane i of the group then receives k0..k0+3 of column
 // n0 + i.  Two such reads give the 8 consecutive k of a KC fragment, so both
@@ -124,9 +85,9 @@ struct McTile {
       const int blk = j * NW + wave;               // 1-KB block of the tile
       const int byte = blk * 1024 + lane * 16;
       const int kr = byte / ROW_BYTES, cp = (byte % ROW_BYTES) >> 4;
-      const int c = cp ^ ((kr & 3) << 2);
+      const int c = cp ^ mc_swz<ROWS>(kr);
       const bool ok = k0 + kr < K && col0 + c * 8 < cols_total;
-      dma16(ok ? p + (int64_t)(k0 + kr) * ld + col0 + c * 8 : g_zero_page, tile + blk * 512);
+      dma16(ok ? p + (int64_t)(k0 + kr) * ld + col0 + c * 8 : zero_page(), tile + blk * 512);
     }
   }
   __device__ __forceinline__ static bf16x8 frag(const bf16_t *tile, int row, int ks, int hl) {
@@ -137,7 +98,7 @@ struct McTile {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int k = ks * 16 + hl * 8 + r * 4 + (s >> 2);
-      const bf16_t *a = tile + k * ROWS + ((((n >> 3) ^ ((k & 3) << 2))) << 3) + (n & 7);
+      const bf16_t *a = tile + k * ROWS + (((n >> 3) ^ mc_swz<ROWS>(k)) << 3) + (n & 7);
       v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(lds_void_t *)a);
     }
     const uint2 lo = __builtin_bit_cast(uint2, v[0]), hi = __builtin_bit_cast(uint2, v[1]);
@@ -398,6 +359,8 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     case 7: return launch<256, 256, 2, 4, 2, LA, LB, EPI>(g, s);
     case 8: return launch<128, 256, 2, 4, 3, LA, LB, EPI>(g, s);
     case 9: return launch<256, 256, 4, 2, 2, LA, LB, EPI>(g, s);
+    case 10: return launch<64, 128, 2, 2, 2, LA, LB, EPI>(g, s);
+    case 11: return launch<128, 64, 2, 2, 2, LA, LB, EPI>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

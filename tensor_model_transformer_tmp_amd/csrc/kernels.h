@@ -54,11 +54,17 @@ int64_t colsum_partial_floats(int rows, int cols);
 hipError_t colsum(bool bf16, const void *x, int rows, int cols, int ldx, float *partial, float *db,
                   int beta, hipStream_t s);
 
+// Row stride of the lse / delta arrays: s rounded up to 64.
+int attn_lse_stride(int s);
+// 0 automatic, 1 split, 2 query-parallel attention kernels (tests, tuning)
+void attention_set_variant(int v);
+
 // Causal attention over QKV [nb*s, 3a] (columns [Q | K | V], head-major):
-// O [nb*s, a], lse [nb, nh, s] (natural log).  bf16, d in {64, 128}.
+// O [nb*s, a], lse [nb, nh, attn_lse_stride(s)] (natural log).  bf16, d in {64, 128}.
 hipError_t attention_fwd(int nb, int s, int nh, int d, int causal, const void *qkv, void *o,
                          float *lse, hipStream_t st);
-// Backward: delta[nb, nh, s] = rowsum(dO * O) workspace; writes dQKV [nb*s, 3a].
+// Backward: delta[nb, nh, attn_lse_stride(s)] = rowsum(dO * O) workspace;
+// writes dQKV [nb*s, 3a].
 hipError_t attention_bwd(int nb, int s, int nh, int d, int causal, const void *qkv,
                          const void *o, const void *dout, const float *lse, float *delta,
                          void *dqkv, hipStream_t st);

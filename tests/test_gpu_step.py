@@ -109,3 +109,26 @@ def test_layer_entry_points_match_schedule_step():
     dev.ctx.sync()
     _bitwise_equal(dev.results(), base)
     dev.close()
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("name", ["pair_d64_ragged", "pair_d128"])
+def test_attention_variants_full_step(variant, name):
+    """Both attention kernel layouts (split and query-parallel) through the
+    whole step, forward and backward, against the oracle with the shard's own
+    outputs visible (zero peers)."""
+    from tensor_model_transformer_tmp_amd import shard
+    cfg = SMALL[name]
+    inp = gen.make_inputs(cfg, zero_peers=True)
+    ref = oschedule.run_step(inp, "serial_fine")
+    shard.set_attention_variant(variant)
+    try:
+        dev = DeviceShard(inp)
+        dev.step("overlap_fine")
+        got = dev.results()
+        dev.step("serial_norecompute")
+        _bitwise_equal(dev.results(), got)
+        dev.close()
+    finally:
+        shard.set_attention_variant(0)
+    _compare(cfg, got, ref, 2e-2)
