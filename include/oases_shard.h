@@ -226,6 +226,11 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
  * Returns OASES_E_ARG for other values. */
 int oases_gemm_tile_variant(int32_t variant);
 
+/* Largest number of workgroups of the AllReduce-point sum kernel for this
+ * process (default 512).  A smaller grid leaves CUs to the other stream's
+ * compute while a sum runs beside it.  1..65536, else OASES_E_ARG. */
+int oases_sum_grid_cap(int32_t workgroups);
+
 /* Attention kernel layout for this process: 0 = automatic (the default),
  * 1 = split (a workgroup owns 32 rows, its waves split the other dimension),
  * 2 = query-parallel (a workgroup owns 128 rows sharing each staged block).

@@ -23,23 +23,47 @@ __device__ __forceinline__ uint4 stream_load(const uint4 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// UNROLL vectors per thread per iteration: their UNROLL * w loads are all in
+// flight before the first add, so a small grid still keeps HBM busy.
+constexpr int SUM_UNROLL = 4;
+
 __global__ void __launch_bounds__(SUM_NT)
     allreduce_bf16_kernel(const uint4 *__restrict__ own, const bf16_t *__restrict__ peers,
                           int64_t peer_stride, int n_peers, uint4 *__restrict__ out, int64_t nvec) {
-  for (int64_t v = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v < nvec;
-       v += (int64_t)gridDim.x * SUM_NT) {
-    const uint4 a = stream_load(own + v);
-    float acc[8] = {lo_f32(a.x), hi_f32(a.x), lo_f32(a.y), hi_f32(a.y),
-                    lo_f32(a.z), hi_f32(a.z), lo_f32(a.w), hi_f32(a.w)};
-    for (int k = 0; k < n_peers; ++k) {
-      const uint4 b = stream_load(reinterpret_cast<const uint4 *>(peers + (int64_t)k * peer_stride) + v);
-      acc[0] += lo_f32(b.x); acc[1] += hi_f32(b.x);
-      acc[2] += lo_f32(b.y); acc[3] += hi_f32(b.y);
-      acc[4] += lo_f32(b.z); acc[5] += hi_f32(b.z);
-      acc[6] += lo_f32(b.w); acc[7] += hi_f32(b.w);
+  const int64_t stride = (int64_t)gridDim.x * SUM_NT;
+  for (int64_t v0 = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v0 < nvec; v0 += stride * SUM_UNROLL) {
+    float acc[SUM_UNROLL][8];
+#pragma unroll
+    for (int u = 0; u < SUM_UNROLL; ++u) {
+      const int64_t v = v0 + u * stride;
+      if (v >= nvec) continue;
+      const uint4 a = stream_load(own + v);
+      acc[u][0] = lo_f32(a.x); acc[u][1] = hi_f32(a.x); acc[u][2] = lo_f32(a.y); acc[u][3] = hi_f32(a.y);
+      acc[u][4] = lo_f32(a.z); acc[u][5] = hi_f32(a.z); acc[u][6] = lo_f32(a.w); acc[u][7] = hi_f32(a.w);
     }
-    out[v] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    for (int k = 0; k < n_peers; ++k) {
+      const uint4 *pk = reinterpret_cast<const uint4 *>(peers + (int64_t)k * peer_stride);
+      uint4 b[SUM_UNROLL];
+#pragma unroll
+      for (int u = 0; u < SUM_UNROLL; ++u) {
+        const int64_t v = v0 + u * stride;
+        b[u] = v < nvec ? stream_load(pk + v) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < SUM_UNROLL; ++u) {
+        acc[u][0] += lo_f32(b[u].x); acc[u][1] += hi_f32(b[u].x);
+        acc[u][2] += lo_f32(b[u].y); acc[u][3] += hi_f32(b[u].y);
+        acc[u][4] += lo_f32(b[u].z); acc[u][5] += hi_f32(b[u].z);
+        acc[u][6] += lo_f32(b[u].w); acc[u][7] += hi_f32(b[u].w);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SUM_UNROLL; ++u) {
+      const int64_t v = v0 + u * stride;
+      if (v >= nvec) continue;
+      out[v] = make_uint4(pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
+                          pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7]));
+    }
   }
 }
 
@@ -127,13 +151,15 @@ __global__ void __launch_bounds__(256)
 
 }  // namespace
 
+int g_sum_grid_cap = 512;  // workgroups of the AllReduce-point sum (tunable)
+
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
                            int n_peers, void *out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t per_vec = bf16 ? 8 : 4;
   const int64_t nvec = n / per_vec;
-  const int64_t want = (nvec + SUM_NT - 1) / SUM_NT;
-  const int grid = (int)(want < 2048 ? want : 2048);
+  const int64_t want = (nvec + SUM_NT * SUM_UNROLL - 1) / (SUM_NT * SUM_UNROLL);
+  const int grid = (int)(want < g_sum_grid_cap ? want : g_sum_grid_cap);
   if (bf16)
     hipLaunchKernelGGL(allreduce_bf16_kernel, dim3(grid), dim3(SUM_NT), 0, s,
                        static_cast<const uint4 *>(own), static_cast<const bf16_t *>(peers),
@@ -144,6 +170,8 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
                        peer_stride, n_peers, static_cast<float4 *>(out), nvec);
   return hipGetLastError();
 }
+
+void allreduce_set_grid_cap(int cap) { g_sum_grid_cap = cap; }
 
 int64_t colsum_partial_floats(int rows, int cols) {
   return (int64_t)((rows + CS_ROWS - 1) / CS_ROWS) * cols;

@@ -423,7 +423,8 @@ int ensure_events(oases_ctx *c) {
   const int n = c->D.L * 2;
   for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB}) {
     v->resize(n, nullptr);
-    for (auto &e : *v) HIPX(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    // device-internal ordering only: no timing, no system-scope fence
+    for (auto &e : *v) HIPX(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence));
   }
   return OASES_OK;
 }
@@ -716,6 +717,12 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
   const hipError_t e = dtype == OASES_BF16 ? gemm_bf16(la, lb, epi, g, static_cast<hipStream_t>(stream))
                                            : gemm_f32(la, lb, epi, g, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? OASES_OK : OASES_E_HIP;
+}
+
+int oases_sum_grid_cap(int32_t workgroups) {
+  if (workgroups < 1 || workgroups > 65536) return OASES_E_ARG;
+  allreduce_set_grid_cap(workgroups);
+  return OASES_OK;
 }
 
 int oases_attention_variant(int32_t variant) {

@@ -47,6 +47,8 @@ void gemm_bf16_set_variant(int v);
 // AllReduce point: out = own + sum_k peers[k] (float32 accumulation in order)
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
                            int n_peers, void *out, int64_t n, hipStream_t s);
+// largest grid (workgroups) of the AllReduce-point kernel
+void allreduce_set_grid_cap(int cap);
 
 // db (+)= column sums of x[rows, cols] in a fixed order; partial needs
 // colsum_partial_floats(rows, cols) floats.

@@ -28,7 +28,7 @@ EXPORTED = ("oases_create", "oases_workspace_bytes", "oases_bind", "oases_set_st
             "layer_fwd", "layer_bwd_recompute", "schedule_step", "oases_schedule_ops",
             "oases_sync", "oases_last_error", "oases_destroy", "oases_profile_begin",
             "oases_profile_end", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
-            "oases_attention_variant", "oases_attention_fwd")
+            "oases_attention_variant", "oases_sum_grid_cap", "oases_attention_fwd")
 
 
 class OasesError(RuntimeError):
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P, I32, I32, P]),
         "oases_gemm_tile_variant": (ctypes.c_int, [I32]),
         "oases_attention_variant": (ctypes.c_int, [I32]),
+        "oases_sum_grid_cap": (ctypes.c_int, [I32]),
         "oases_attention_fwd": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -260,6 +261,10 @@ def gemm_fwd(dtype, a, b, c, bias=None, gelu=False, pre=None, stream=None):
 
 def set_gemm_tile_variant(v: int):
     _check_free(lib().oases_gemm_tile_variant(v), "oases_gemm_tile_variant")
+
+
+def set_sum_grid_cap(workgroups: int):
+    _check_free(lib().oases_sum_grid_cap(workgroups), "oases_sum_grid_cap")
 
 
 def set_attention_variant(v: int):
