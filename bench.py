@@ -59,28 +59,43 @@ def step_flops(cfg):
     return 2 * f, 2 * r, 2 * b
 
 
-def sum_bytes(cfg):
-    """HBM bytes of all AllReduce-point sums of a step: (w+1) T h elements per point."""
-    esz = 2 if cfg.dtype == gen.BF16 else 4
-    return 2 * 2 * cfg.n_layers * (cfg.tmp_width + 1) * cfg.t_sb * cfg.hidden * esz
+# Algorithmic work of one launch of each kernel class (averaged over the
+# class's launches in a step).  A class is what the executor brackets with one
+# pair of HIP events: one GEMM, one attention forward, one attention backward
+# (delta + dK/dV + dQ kernels), one AllReduce-point sum, one bias column sum.
+KERNEL_CLASSES = ("gemm_fwd", "gemm_dx", "gemm_dw", "attn_fwd", "attn_bwd", "sum", "colsum")
 
 
-# flops of one launch of each GEMM kind (for the dominant-kernel roofline)
-def gemm_class_flops(cfg, kclass):
+def class_launches(cfg, kclass):
+    """Launches of a kernel class in one overlapped fine-grained step."""
+    L = cfg.n_layers
+    n_attn = sum(1 for b in cfg.blocks if b == gen.ATTN)
+    return {"gemm_fwd": 6 * L, "gemm_dx": 4 * L, "gemm_dw": 4 * L, "attn_fwd": 4 * n_attn, "attn_bwd": 2 * n_attn,
+            "sum": 4 * L, "colsum": 2 * L}[kclass]
+
+
+def class_work(cfg, kclass):
+    """(algorithmic work of one step for the class, unit): FLOPs or HBM bytes."""
     T, h = cfg.t_sb, cfg.hidden
+    esz = 2 if cfg.dtype == gen.BF16 else 4
     tot = 0.0
     for l, kind in enumerate(cfg.blocks):
         nin, nmid = cfg.n_in(l), cfg.n_mid(l)
-        if kclass == "gemm_fwd":   # F: column + row, R: column (per sub-batch)
-            tot += 2 * (2 * gemm_flops(T, nin, h) + gemm_flops(T, h, nmid))
+        col, row = gemm_flops(T, nin, h), gemm_flops(T, h, nmid)
+        att = attn_matmul_flops(cfg) if kind == gen.ATTN else 0.0
+        if kclass == "gemm_fwd":     # F: column + row, R: column
+            tot += 2 * (2 * col + row)
         elif kclass in ("gemm_dx", "gemm_dw"):
-            tot += 2 * (gemm_flops(T, nin, h) + gemm_flops(T, h, nmid))
-    return tot
-
-
-def gemm_class_launches(cfg, kclass):
-    L = cfg.n_layers
-    return {"gemm_fwd": 6 * L, "gemm_dx": 4 * L, "gemm_dw": 4 * L}[kclass]
+            tot += 2 * (col + row)
+        elif kclass == "attn_fwd":   # F and R: QK^T and PV
+            tot += 2 * 2 * 2 * att
+        elif kclass == "attn_bwd":   # dV, dP, dQ, dK
+            tot += 2 * 4 * att
+        elif kclass == "sum":
+            tot += 2 * 2 * (cfg.tmp_width + 1) * T * h * esz
+        elif kclass == "colsum":     # read dpre once, read-modify-write db
+            tot += 2 * (T * nin * esz + 2 * nin * 4)
+    return tot, ("B" if kclass in ("sum", "colsum") else "FLOP")
 
 
 # ---------------------------------------------------------------------------
@@ -95,7 +110,7 @@ def cpu_baseline(cfg, budget_s=12.0):
     while True:
         schedule.run_step(inp, "serial_fine")
         n += 1
-        if time.perf_counter() - t0 >= budget_s or n >= 20:
+        if time.perf_counter() - t0 >= budget_s or n >= 200:
             break
     dt = (time.perf_counter() - t0) / n
     cores = len(os.sched_getaffinity(0))
@@ -105,6 +120,40 @@ def cpu_baseline(cfg, budget_s=12.0):
                       f"on {cores} threads"}
 
 
+def stored_traffic(kclass, workload):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) stored
+    from two counter runs of this bench, or None when absent or when the
+    kernel sources have changed since the counters were taken."""
+    from tensor_model_transformer_tmp_amd.rocprof_summary import sources_hash
+    path = os.path.join(ROOT, "profiles", f"{kclass}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for ln in fh:
+            k, sep, v = ln.partition(":")
+            if sep:
+                kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256") != sources_hash(kclass):
+        return None
+    return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+
+
+def copy_calibration(nbytes):
+    """A plain copy of known size (the sum kernel with no peers), for scaling
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    from tensor_model_transformer_tmp_amd import shard
+    n = nbytes // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        shard.allreduce_point(shard.BF16, src, src, 0, dst)
+    torch.cuda.synchronize()
+    assert bool((dst == 1).all())
+    print(json.dumps({"copy_bytes": 2 * n, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,9 +161,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD, choices=gen.PRESET_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--roofline-kernel", default="gemm_fwd",
-                    choices=["gemm_fwd", "gemm_dx", "gemm_dw", "sum"])
+    ap.add_argument("--roofline-kernel", default=None, choices=list(KERNEL_CLASSES),
+                    help="kernel class for the roofline entry (default: most time per step)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES three times (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
         print(f"bench.py runs one GPU's TMP shard; --gpus {args.gpus} is not supported "
               "(the AllReduce points are emulated with resident peer buffers on one GPU)",
@@ -151,36 +204,50 @@ def main():
     sec = timed("overlap_fine", use_graph, args.steps, args.warmup)
     sec_serial = timed("serial_fine", use_graph, max(5, args.steps // 2), 3)
 
-    # dominant-kernel and sum-kernel timing: eager steps with HIP events on the launch stream
+    # Per-kernel-class timing: eager overlapped steps with a pair of HIP events
+    # recorded on the kernel's own launch stream around every launch of the class.
     def class_time(kclass, steps):
-        dev.ctx.profile_begin(kclass, 8192)
+        dev.ctx.profile_begin(kclass, 16384)
         run("overlap_fine", False, steps)
         ms, n = dev.ctx.profile_end()
         return ms / 1e3, n
 
     prof_steps = max(3, min(args.steps, 20))
-    k = args.roofline_kernel
-    k_sec, k_n = class_time(k, prof_steps)
-    sum_sec, sum_n = class_time("sum", prof_steps)
+    kernels = {}
+    for kc in KERNEL_CLASSES:
+        work, unit = class_work(cfg, kc)
+        if work == 0:
+            continue
+        t, n = class_time(kc, prof_steps)
+        per_step = n // prof_steps
+        assert per_step == class_launches(cfg, kc), (kc, n, prof_steps)
+        avg = t / n
+        if unit == "FLOP":
+            ach, pk, u = work / per_step / avg / 1e12, (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == gen.BF16
+                                                        else FP32_PEAK_TFLOPS), "TFLOP/s"
+        else:
+            ach, pk, u = work / per_step / avg / 1e9, HBM_PEAK_GBS, "GB/s"
+        kernels[kc] = {"launches_per_step": per_step, "avg_us": avg * 1e6,
+                       "us_per_step": t / prof_steps * 1e6, "achieved": ach, "unit": u,
+                       "frac": ach / pk, "work_per_launch": work / per_step,
+                       "work_unit": unit}
     dev.close()
 
     f, r, b = step_flops(cfg)
     flops = f + r + b
     value = flops / sec / 1e12
-    sum_per_step = sum_sec / prof_steps
+    sum_per_step = kernels["sum"]["us_per_step"] / 1e6
     hidden = (sec_serial - sec) / sum_per_step if sum_per_step > 0 else None
-    if k == "sum":
-        per_launch = sum_bytes(cfg) / (4 * cfg.n_layers)
-        achieved = per_launch / (k_sec / k_n) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
-    else:
-        per_launch = gemm_class_flops(cfg, k) / gemm_class_launches(cfg, k)
-        achieved = per_launch / (k_sec / k_n) / 1e12
-        peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == gen.BF16 else FP32_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None}
-    roof["kernel"] = f"{k} ({k_n} launches timed over {prof_steps} eager steps)"
+    k = args.roofline_kernel or max(kernels, key=lambda c: kernels[c]["us_per_step"])
+    kk = kernels[k]
+    hbm = kk["unit"] == "GB/s"
+    roof = {"bound": "hbm" if hbm else "mfma", "achieved": kk["achieved"],
+            "peak": HBM_PEAK_GBS if hbm else (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == gen.BF16
+                                              else FP32_PEAK_TFLOPS),
+            "unit": kk["unit"], "frac": kk["frac"], "traffic": stored_traffic(k, cfg.name),
+            "kernel": f"{k}: {kk['launches_per_step'] * prof_steps} launches over {prof_steps} "
+                      f"eager overlapped steps, avg {kk['avg_us']:.2f} us, "
+                      f"{kk['work_per_launch']:.4g} {kk['work_unit']} per launch"}
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -199,7 +266,7 @@ def main():
         "serial_ms_per_step": sec_serial * 1e3,
         "launch_probe_ms": {"eager": launch[False] * 1e3, "graph": launch[True] * 1e3},
         "sum_ms_per_step": sum_per_step * 1e3,
-        "sum_hbm_gbs": sum_bytes(cfg) / sum_per_step / 1e9 if sum_per_step > 0 else None,
+        "kernels": kernels,
         "gflop_per_step": {"fwd": f / 1e9, "recompute": r / 1e9, "bwd": b / 1e9},
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(cfg),

@@ -189,9 +189,12 @@ void oases_destroy(oases_ctx *c);
  * 1 GEMM data gradient, 2 GEMM weight gradient, 3 attention forward,
  * 4 attention backward, 5 AllReduce-point sum, 6 bias-gradient column sum).
  * After oases_profile_begin, every eager (not graph-captured) launch of that
- * class is bracketed by HIP events on the stream it is launched on, for at
- * most max_launches launches.  oases_profile_end waits for those events and
- * returns the summed kernel time and the number of launches timed. */
+ * class, for at most max_launches launches, is timed by a pair of HIP events
+ * carried in the dispatch packets of its kernels (hipExtLaunchKernelGGL):
+ * from the start of its first kernel to the end of its last, on the stream
+ * it is launched on.  oases_profile_end waits for those events and returns
+ * the summed time and the number of launches timed.  Timing state is per
+ * host thread. */
 int oases_profile_begin(oases_ctx *c, int32_t kernel_class, int32_t max_launches);
 int oases_profile_end(oases_ctx *c, double *total_ms, int32_t *launches);
 

@@ -948,12 +948,12 @@ hipError_t fwd_d(int nb, int s, int nh, int causal, const void *qkv, void *o, fl
   const float scale_log2 = LOG2E / sqrtf((float)D);
   if (use_qp(s, nb * nh)) {
     dim3 grid((s + 32 * QP_NW - 1) / (32 * QP_NW), nb * nh);
-    hipLaunchKernelGGL((attn_fwd_qp_kernel<D, 3>), grid, dim3(64 * QP_NW), 0, st,
+    OASES_LAUNCH((attn_fwd_qp_kernel<D, 3>), grid, dim3(64 * QP_NW), st,
                        static_cast<const bf16_t *>(qkv), static_cast<bf16_t *>(o), lse, s, attn_lse_stride(s),
                        nh, causal, scale_log2);
   } else {
     dim3 grid((s + 31) / 32, nb * nh);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, 3>), grid, dim3(64 * Split<D>::NW), 0, st,
+    OASES_LAUNCH((attn_fwd_kernel<D, 3>), grid, dim3(64 * Split<D>::NW), st,
                        static_cast<const bf16_t *>(qkv), static_cast<bf16_t *>(o), lse, s, attn_lse_stride(s),
                        nh, causal, scale_log2);
   }
@@ -965,7 +965,7 @@ hipError_t bwd_d(int nb, int s, int nh, int causal, const void *qkv, const void 
                  const float *lse, float *delta, void *dqkv, hipStream_t st) {
   const int s_pad = attn_lse_stride(s);
   const int64_t rows = (int64_t)nb * s * nh;
-  hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+  OASES_LAUNCH(attn_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), st,
                      static_cast<const bf16_t *>(o), static_cast<const bf16_t *>(dout), delta, nb, s, s_pad, nh);
   const float scale = 1.f / sqrtf((float)D), scale_log2 = scale * LOG2E;
   const bf16_t *q = static_cast<const bf16_t *>(qkv), *d_o = static_cast<const bf16_t *>(dout);
@@ -973,15 +973,15 @@ hipError_t bwd_d(int nb, int s, int nh, int causal, const void *qkv, const void 
   if (use_qp(s, nb * nh)) {
     dim3 grid((s + 32 * QP_NW - 1) / (32 * QP_NW), nb * nh);
     constexpr int KV_STAGES = D == 128 ? 2 : 3;
-    hipLaunchKernelGGL((attn_bwd_dkdv_qp_kernel<D, KV_STAGES>), grid, dim3(64 * QP_NW), 0, st, q, d_o, lse,
+    OASES_LAUNCH((attn_bwd_dkdv_qp_kernel<D, KV_STAGES>), grid, dim3(64 * QP_NW), st, q, d_o, lse,
                        delta, dq, s, s_pad, nh, causal, scale_log2, scale);
-    hipLaunchKernelGGL((attn_bwd_dq_qp_kernel<D, 3>), grid, dim3(64 * QP_NW), 0, st, q, d_o, lse, delta, dq, s,
+    OASES_LAUNCH((attn_bwd_dq_qp_kernel<D, 3>), grid, dim3(64 * QP_NW), st, q, d_o, lse, delta, dq, s,
                        s_pad, nh, causal, scale_log2, scale);
   } else {
     dim3 grid((s + 31) / 32, nb * nh);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, 2>), grid, dim3(64 * Split<D>::NW), 0, st, q, d_o, lse, delta,
+    OASES_LAUNCH((attn_bwd_dkdv_kernel<D, 2>), grid, dim3(64 * Split<D>::NW), st, q, d_o, lse, delta,
                        dq, s, s_pad, nh, causal, scale_log2, scale);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, 3>), grid, dim3(64 * Split<D>::NW), 0, st, q, d_o, lse, delta, dq,
+    OASES_LAUNCH((attn_bwd_dq_kernel<D, 3>), grid, dim3(64 * Split<D>::NW), st, q, d_o, lse, delta, dq,
                        s, s_pad, nh, causal, scale_log2, scale);
   }
   return hipGetLastError();

@@ -161,11 +161,11 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
   const int64_t want = (nvec + SUM_NT * SUM_UNROLL - 1) / (SUM_NT * SUM_UNROLL);
   const int grid = (int)(want < g_sum_grid_cap ? want : g_sum_grid_cap);
   if (bf16)
-    hipLaunchKernelGGL(allreduce_bf16_kernel, dim3(grid), dim3(SUM_NT), 0, s,
+    OASES_LAUNCH(allreduce_bf16_kernel, dim3(grid), dim3(SUM_NT), s,
                        static_cast<const uint4 *>(own), static_cast<const bf16_t *>(peers),
                        peer_stride, n_peers, static_cast<uint4 *>(out), nvec);
   else
-    hipLaunchKernelGGL(allreduce_f32_kernel, dim3(grid), dim3(SUM_NT), 0, s,
+    OASES_LAUNCH(allreduce_f32_kernel, dim3(grid), dim3(SUM_NT), s,
                        static_cast<const float4 *>(own), static_cast<const float *>(peers),
                        peer_stride, n_peers, static_cast<float4 *>(out), nvec);
   return hipGetLastError();
@@ -184,11 +184,11 @@ hipError_t colsum(bool bf16, const void *x, int rows, int cols, int ldx, float *
   if (nchunks > 0) {
     dim3 g1((cols + 255) / 256, nchunks);
     if (bf16)
-      hipLaunchKernelGGL(colsum_pass1<true>, g1, dim3(256), 0, s, x, rows, cols, ldx, partial);
+      OASES_LAUNCH(colsum_pass1<true>, g1, dim3(256), s, x, rows, cols, ldx, partial);
     else
-      hipLaunchKernelGGL(colsum_pass1<false>, g1, dim3(256), 0, s, x, rows, cols, ldx, partial);
+      OASES_LAUNCH(colsum_pass1<false>, g1, dim3(256), s, x, rows, cols, ldx, partial);
   }
-  hipLaunchKernelGGL(colsum_pass2, dim3((cols + 31) / 32), dim3(256), 0, s, partial, nchunks, cols, db,
+  OASES_LAUNCH(colsum_pass2, dim3((cols + 31) / 32), dim3(256), s, partial, nchunks, cols, db,
                      beta);
   return hipGetLastError();
 }

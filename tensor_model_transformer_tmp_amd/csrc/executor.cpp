@@ -26,6 +26,13 @@
 
 using namespace oases;
 
+namespace oases {
+LaunchTimer &launch_timer() {
+  static thread_local LaunchTimer t;
+  return t;
+}
+}  // namespace oases
+
 namespace {
 
 enum OpKind : int32_t { OP_F = 0, OP_CF = 1, OP_R = 2, OP_CR = 3, OP_BDX = 4, OP_CB = 5, OP_BDW = 6 };
@@ -247,17 +254,19 @@ struct Exec {
     return static_cast<const char *>(p) + (size_t)(l * 2 + sb) * per;
   }
 
-  int prof_begin(int cls, hipStream_t s) {
+  // Time one launch of kernel class `cls`: arm the next event pair, which the
+  // kernels launched until prof_end carry in their dispatch packets.
+  int prof_begin(int cls, hipStream_t) {
     if (c->prof_class != cls || c->capturing) return OASES_OK;
     if (c->prof_used + 2 > c->prof_ev.size()) return OASES_OK;  // ring full: stop timing
-    HIPX(hipEventRecord(c->prof_ev[c->prof_used], s));
+    launch_timer() = LaunchTimer{c->prof_ev[c->prof_used], c->prof_ev[c->prof_used + 1]};
     return OASES_OK;
   }
-  int prof_end(int cls, hipStream_t s) {
+  int prof_end(int cls, hipStream_t) {
     if (c->prof_class != cls || c->capturing) return OASES_OK;
-    if (c->prof_used + 2 > c->prof_ev.size()) return OASES_OK;
-    HIPX(hipEventRecord(c->prof_ev[c->prof_used + 1], s));
-    c->prof_used += 2;
+    const bool launched = launch_timer().stop && !launch_timer().start;  // a kernel took the pair
+    launch_timer() = LaunchTimer{};
+    if (launched) c->prof_used += 2;
     return OASES_OK;
   }
 
@@ -647,9 +656,10 @@ int oases_profile_begin(oases_ctx *c, int32_t kernel_class, int32_t max_launches
     return set_err(c, OASES_E_ARG, "bad kernel class or launch count");
   for (auto &e : c->prof_ev) if (e) (void)hipEventDestroy(e);
   c->prof_ev.assign((size_t)max_launches * 2, nullptr);
-  for (auto &e : c->prof_ev) HIPX(hipEventCreate(&e));
+  for (auto &e : c->prof_ev) HIPX(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   c->prof_used = 0;
   c->prof_class = kernel_class;
+  launch_timer() = LaunchTimer{};
   return OASES_OK;
 }
 
@@ -666,6 +676,7 @@ int oases_profile_end(oases_ctx *c, double *total_ms, int32_t *launches) {
   *launches = (int32_t)(c->prof_used / 2);
   c->prof_class = -1;
   c->prof_used = 0;
+  launch_timer() = LaunchTimer{};
   return OASES_OK;
 }
 

@@ -328,8 +328,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
 template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI>
 hipError_t launch(const GemmArgs &g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, LA, LB, EPI>), dim3(tiles),
-                     dim3(64 * WGM * WGN), 0, s, g);
+  OASES_LAUNCH((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, LA, LB, EPI>), dim3(tiles),
+                     dim3(64 * WGM * WGN), s, g);
   return hipGetLastError();
 }
 
@@ -340,12 +340,16 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
   int v = g_variant;
   if (v == 0) {
     // measured on MI355X over the workload shapes: 256x256 (8 waves) when it
-    // alone gives a tile per CU, 128x256 (8 waves) near that, otherwise
-    // 128x128 tiles (3 stages for long k loops, 2 stages / 2 per CU for short)
+    // alone gives a tile per CU, 128x256 (8 waves) near that; 128x128 tiles
+    // (3 stages for long k loops, 2 stages for short) while they still give
+    // a tile per CU, and below that 64x128 tiles (128x64 for a weight
+    // gradient wider than it is tall)
     const int64_t t256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
     const int64_t t128x256 = (int64_t)((g.M + 127) / 128) * ((g.N + 255) / 256);
+    const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
     if (t256 >= 256) v = 9;
     else if (t128x256 >= 192) v = 8;
+    else if (t128 < 256) v = LA == MC && g.M < g.N ? 11 : 10;
     else if (g.K >= 2048) v = 2;
     else v = 5;
   }

@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
 template <Layout LA, Layout LB, int EPI>
 hipError_t launch(const GemmArgs &g, hipStream_t s) {
   dim3 grid((g.N + TB - 1) / TB, (g.M + TB - 1) / TB);
-  hipLaunchKernelGGL((gemm_f32_kernel<LA, LB, EPI>), grid, dim3(256), 0, s, g);
+  OASES_LAUNCH((gemm_f32_kernel<LA, LB, EPI>), grid, dim3(256), s, g);
   return hipGetLastError();
 }
 

@@ -3,10 +3,42 @@
 // the caller (executor / C-ABI entry points) before any launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace oases {
+
+// Kernel timing.  While a pair of events is armed (the executor arms one pair
+// around each launch of the kernel class being timed), launches carry the
+// events in their own dispatch packets: the start event takes the start time
+// of the first kernel launched, the stop event the end time of every kernel
+// launched (the last one wins).  The pair therefore spans exactly the class's
+// kernels, with no marker packets of its own in the stream.
+struct LaunchTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTimer &launch_timer();  // per host thread
+
+template <class K, class... Args>
+inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  LaunchTimer &t = launch_timer();
+  if (t.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start, t.stop, 0, args...);
+    t.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+  return hipGetLastError();
+}
+
+// launch through launch_kernel and return its error from the enclosing function
+#define OASES_LAUNCH(kernel, grid, block, stream, ...)                                    \
+  do {                                                                                   \
+    if (hipError_t oases_launch_err_ = ::oases::launch_kernel(kernel, grid, block, stream, \
+                                                              __VA_ARGS__))              \
+      return oases_launch_err_;                                                          \
+  } while (0)
 
 // GEMM epilogues
 enum Epi : int {
