@@ -234,10 +234,11 @@ int oases_gemm_tile_variant(int32_t variant);
  * compute while a sum runs beside it.  1..65536, else OASES_E_ARG. */
 int oases_sum_grid_cap(int32_t workgroups);
 
-/* Attention kernel layout for this process: 0 = automatic (the default),
- * 1 = split (a workgroup owns 32 rows, its waves split the other dimension),
- * 2 = query-parallel (a workgroup owns 128 rows sharing each staged block).
- * For tests and tuning; OASES_E_ARG for other values. */
+/* Attention work split for this process.  A workgroup has 4 waves of 32
+ * rows each; OWN of them own distinct row tiles (sharing each staged block)
+ * and 4/OWN split the walk over the other operand.  0 = automatic (the
+ * default: the largest OWN that gives 256 workgroups), 1 = OWN 1, 2 = OWN 4,
+ * 3 = OWN 2.  For tests and tuning; OASES_E_ARG for other values. */
 int oases_attention_variant(int32_t variant);
 
 /* Causal (causal = 1) or full attention forward over QKV [nb*s, 3a]

@@ -111,7 +111,7 @@ def test_layer_entry_points_match_schedule_step():
     dev.close()
 
 
-@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("variant", [1, 2, 3])
 @pytest.mark.parametrize("name", ["pair_d64_ragged", "pair_d128"])
 def test_attention_variants_full_step(variant, name):
     """Both attention kernel layouts (split and query-parallel) through the
