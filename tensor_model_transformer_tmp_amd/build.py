@@ -25,9 +25,17 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wno-unused-command-line-argument", "-I" + os.path.join(ROOT, "include")]
 
 
+# per-source additions.  attention.hip: MFMA results in arch VGPRs, so the
+# softmax arithmetic on score tiles needs no moves between AGPRs and VGPRs
+# (and the kernels need far fewer registers).  The GEMM source does not build
+# with this option in this toolchain, and its accumulators are only read
+# once, in the epilogue.
+EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

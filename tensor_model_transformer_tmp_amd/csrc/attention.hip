@@ -83,14 +83,41 @@ __device__ __forceinline__ float other_half(float x) {
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Make the compiler wait for (and keep) values loaded from global memory
+// before the walk starts.  The LDS DMA is invisible to the compiler's wait
+// counting, so a load still outstanding at the loop would otherwise be waited
+// for inside the loop with a vmcnt that also drains the prefetch DMA.
+__device__ __forceinline__ void settle(const bf16x8 &v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  asm volatile("" ::"v"(u));
+}
+__device__ __forceinline__ void settle(float v) { asm volatile("" ::"v"(v)); }
+
+// LDS byte address of a shared-memory pointer (one address-space cast; the
+// DMA helpers below take 32-bit LDS addresses so that per-unit address
+// arithmetic stays in 32-bit scalar registers).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)p);
+}
+
 // DMA of one 1-KB unit with a scalar base and a per-lane 32-bit byte offset
 // (global_load_lds_dwordx4 v_off, s[base]): the 64 lanes' 16 bytes land
-// contiguously at LDS address dst.
-__device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, const void *dst) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)dst;
+// contiguously at LDS byte address lds.
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;  // uniform; made scalar explicitly
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sb)
+               : "m0", "memory");
+}
+// the same with a per-lane 64-bit source address
+__device__ __forceinline__ void dma16_v(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
                : "m0", "memory");
 }
 
@@ -139,23 +166,6 @@ struct Blk {
     return as_frag(make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
 };
-
-// DMA of unit u of the block whose first row is row0 of a [rows x ld] matrix
-// at p: a full block uses the precomputed lane offset and a scalar base; a
-// block reaching past the last row clamps its rows to the last one (those
-// rows are masked out of every result).
-template <int D>
-__device__ __forceinline__ void dma_block_unit(const bf16_t *p, int ld, int row0, int rows, int u,
-                                               uint32_t voff, bf16_t *dst, int lane) {
-  if (row0 + RB <= rows) {
-    dma16_s(p + (int64_t)row0 * ld, voff, dst);
-  } else {
-    int r, cb;
-    Blk<D>::unit_src(u, lane, r, cb);
-    const int row = min(row0 + r, rows - 1);
-    dma16(p + (int64_t)row * ld + (cb >> 1), dst);
-  }
-}
 
 // Walk steps 0..nst-1 through a ring of STAGES LDS slots.  issue(i, slot)
 // starts the DMA of step i (exactly DL DMA instructions per wave);
@@ -230,6 +240,50 @@ struct KvCfg {  // staging of K and V blocks (forward and dQ)
   static constexpr int LDS = STAGES * STAGE_BYTES > RED_BYTES ? STAGES * STAGE_BYTES : RED_BYTES;
 };
 
+// Clamped DMA of one unit whose full-block source is base + voff bytes in a
+// [rows x ld] matrix starting at row row0: rows past the last one read the
+// last row (such rows are masked out of every result).
+__device__ __forceinline__ void dma_clamped(const bf16_t *p, int ld, int row0, int rows, uint32_t voff,
+                                            uint32_t lds) {
+  const uint32_t e = voff >> 1, r = e / (uint32_t)ld, col = e - r * (uint32_t)ld;
+  const int row = min(row0 + (int)r, rows - 1);
+  dma16_v(p + (int64_t)row * ld + col, lds);
+}
+
+// K and V of SPLIT consecutive key blocks per step.  Unit uu = j*NW + wave of
+// a step is block g = uu / (2 UNITS), K or V, unit uu % UNITS of that block.
+// Lane offsets are relative to the step's first key row, so all units of a
+// step share one scalar base and a unit costs a DMA and an M0 write.
+template <int D, int OWN>
+struct KvStager {
+  using B = Blk<D>;
+  using C = KvCfg<D, OWN>;
+  uint32_t voff[C::DL];
+  int lds[C::DL];  // byte offset of the unit in a stage (uniform)
+  __device__ __forceinline__ void init(int wave, int lane, int ld, int a) {
+#pragma unroll
+    for (int j = 0; j < C::DL; ++j) {
+      const int uu = j * NW + wave, g = uu / (2 * B::UNITS), which = (uu / B::UNITS) & 1, u = uu % B::UNITS;
+      int r, cb;
+      B::unit_src(u, lane, r, cb);
+      voff[j] = (uint32_t)(((g * RB + r) * ld + which * a) * 2 + cb);
+      lds[j] = (g * 2 + which) * B::BYTES + u * 1024;
+    }
+  }
+  // key rows [row0, row0 + SPLIT*RB) of K (V at column offset a) at Kp
+  // stage: LDS byte address of the stage
+  __device__ __forceinline__ void issue(const bf16_t *Kp, int ld, int s, int row0, uint32_t stage) const {
+    if (row0 + C::SPLIT * RB <= s) {
+      const bf16_t *base = Kp + (int64_t)row0 * ld;
+#pragma unroll
+      for (int j = 0; j < C::DL; ++j) dma16_s(base, voff[j], stage + lds[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::DL; ++j) dma_clamped(Kp, ld, row0, s, voff[j], stage + lds[j]);
+    }
+  }
+};
+
 template <int D, int OWN>
 __global__ void __launch_bounds__(64 * NW)
     attn_fwd_kernel(const bf16_t *__restrict__ qkv, bf16_t *__restrict__ out, float *__restrict__ lse,
@@ -249,21 +303,16 @@ __global__ void __launch_bounds__(64 * NW)
   const bf16_t *Qp = qkv + (int64_t)b * s * ld + h * D;
   const bf16_t *Kp = Qp + a;
 
-  // lane offsets of this wave's DMA units: unit uu = j*NW + wave of a step is
-  // block uu / (2 UNITS) of the step, K (0) or V (1), unit uu % UNITS of that block
-  uint32_t voff[DL];
-#pragma unroll
-  for (int j = 0; j < DL; ++j) {
-    int r, cb;
-    B::unit_src((j * NW + wave) % B::UNITS, lane, r, cb);
-    voff[j] = (uint32_t)(r * ld * 2 + cb);  // the V column offset is in the base pointer
-  }
+  KvStager<D, OWN> stg;
+  stg.init(wave, lane, ld, a);
 
   bf16x8 qf[D / 16];
   {
     const int qrow = min(qi, s - 1);  // rows past the end compute on a real row; never stored
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = load_frag(Qp + (int64_t)qrow * ld + kk * 16 + hl * 8);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) settle(qf[kk]);
   }
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -275,15 +324,8 @@ __global__ void __launch_bounds__(64 * NW)
   const int nkb = (kend + RB - 1) / RB;
   const int nst = (nkb + SPLIT - 1) / SPLIT;
 
-  auto issue = [&](int st, int slot) {
-    char *base = smem + slot * C::STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < DL; ++j) {
-      const int uu = j * NW + wave, g = uu / (2 * B::UNITS), which = (uu / B::UNITS) & 1, u = uu % B::UNITS;
-      bf16_t *dst = reinterpret_cast<bf16_t *>(base + (g * 2 + which) * B::BYTES + u * 1024);
-      dma_block_unit<D>(Kp + which * a, ld, (st * SPLIT + g) * RB, s, u, voff[j], dst, lane);
-    }
-  };
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int st, int slot) { stg.issue(Kp, ld, s, st * SPLIT * RB, smem_lds + slot * C::STAGE_BYTES); };
   auto compute = [&](int st, int slot) {
     const int kb = st * SPLIT + sp, k0 = kb * RB;
     if (kb >= nkb || (causal && k0 > qw0 + 31)) return;
@@ -407,14 +449,61 @@ __global__ void __launch_bounds__(256)
 template <int D, int OWN>
 struct DkdvCfg {
   static constexpr int SPLIT = NW / OWN;
-  static constexpr int PB = 2 * Blk<D>::UNITS + 1;                 // Q, dO, lse+delta
-  static constexpr int UNITS = (SPLIT * PB + NW - 1) / NW * NW;   // padded to whole waves
-  static constexpr int DL = UNITS / NW;
+  static constexpr int QU = SPLIT * Blk<D>::UNITS / NW;  // Q units per wave per step (dO: as many)
+  static_assert(SPLIT * Blk<D>::UNITS % NW == 0, "units per wave");
+  static constexpr int DL = 2 * QU + 1;                   // + one lse/delta (or padding) unit
   static constexpr int BLOCK_BYTES = 2 * Blk<D>::BYTES + 1024;
   static constexpr int STAGE_BYTES = SPLIT * BLOCK_BYTES + 1024;  // + a sink for padding units
   static constexpr int STAGES = 3 * STAGE_BYTES <= LDS_BUDGET ? 3 : 2;
   static constexpr int RED_BYTES = NW * D * 32 * 4;
   static constexpr int LDS = STAGES * STAGE_BYTES > RED_BYTES ? STAGES * STAGE_BYTES : RED_BYTES;
+};
+
+// Q and dO of SPLIT consecutive query blocks per step, and their lse and
+// delta.  Q unit j of a wave is unit qu = j*NW + wave of the step (block
+// qu / UNITS); dO units likewise; wave w < SPLIT also stages the lse (lanes
+// 0-7) and delta (lanes 8-15) of block w, other waves a padding unit, so
+// every wave issues DL units per step.
+template <int D, int OWN>
+struct DkdvStager {
+  using B = Blk<D>;
+  using C = DkdvCfg<D, OWN>;
+  uint32_t qoff[C::QU], ooff[C::QU];
+  int qlds[C::QU];  // byte offset of Q unit j in a stage (its dO unit: + B::BYTES)
+  __device__ __forceinline__ void init(int wave, int lane, int ld, int a) {
+#pragma unroll
+    for (int j = 0; j < C::QU; ++j) {
+      const int qu = j * NW + wave, g = qu / B::UNITS, u = qu % B::UNITS;
+      int r, cb;
+      B::unit_src(u, lane, r, cb);
+      qoff[j] = (uint32_t)((g * RB + r) * ld * 2 + cb);
+      ooff[j] = (uint32_t)((g * RB + r) * a * 2 + cb);
+      qlds[j] = g * C::BLOCK_BYTES + u * 1024;
+    }
+  }
+  // query rows [row0, row0 + SPLIT*RB); stage: LDS byte address of the stage
+  __device__ __forceinline__ void issue(const bf16_t *Qp, const bf16_t *dOp, const float *lp, const float *dlp,
+                                        int ld, int a, int s, int s_pad, int row0, uint32_t stage, int wave,
+                                        int lane) const {
+    if (row0 + C::SPLIT * RB <= s) {
+      const bf16_t *bq = Qp + (int64_t)row0 * ld, *bo = dOp + (int64_t)row0 * a;
+#pragma unroll
+      for (int j = 0; j < C::QU; ++j) dma16_s(bq, qoff[j], stage + qlds[j]);
+#pragma unroll
+      for (int j = 0; j < C::QU; ++j) dma16_s(bo, ooff[j], stage + qlds[j] + B::BYTES);
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::QU; ++j) dma_clamped(Qp, ld, row0, s, qoff[j], stage + qlds[j]);
+#pragma unroll
+      for (int j = 0; j < C::QU; ++j) dma_clamped(dOp, a, row0, s, ooff[j], stage + qlds[j] + B::BYTES);
+    }
+    if (wave < C::SPLIT) {  // lse and delta rows are padded to s_pad
+      const int i = lane & 15, r = min(row0 + wave * RB, s_pad - RB) + 4 * (i & 7);
+      dma16_v((i < 8 ? lp : dlp) + r, stage + wave * C::BLOCK_BYTES + 2 * B::BYTES);
+    } else {
+      dma16_v(zero_page(), stage + C::SPLIT * C::BLOCK_BYTES);
+    }
+  }
 };
 
 template <int D, int OWN>
@@ -425,7 +514,7 @@ __global__ void __launch_bounds__(64 * NW)
                      float scale) {
   using B = Blk<D>;
   using C = DkdvCfg<D, OWN>;
-  constexpr int SPLIT = C::SPLIT, DL = C::DL, PB = C::PB;
+  constexpr int SPLIT = C::SPLIT, DL = C::DL;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
@@ -439,16 +528,8 @@ __global__ void __launch_bounds__(64 * NW)
   const bf16_t *dOp = dout + (int64_t)b * s * a + h * D;
   const float *lp = lse + (int64_t)bh * s_pad, *dlp = delta + (int64_t)bh * s_pad;
 
-  // unit uu = j*NW + wave of a step: block uu / PB, within it the Q units,
-  // the dO units, then the lse/delta unit; units past SPLIT*PB are padding
-  uint32_t voff[DL];
-#pragma unroll
-  for (int j = 0; j < DL; ++j) {
-    const int uu = j * NW + wave, v = uu % PB;
-    int r = 0, cb = 0;
-    if (v < 2 * B::UNITS) B::unit_src(v % B::UNITS, lane, r, cb);
-    voff[j] = (uint32_t)(r * (v < B::UNITS ? ld : a) * 2 + cb);
-  }
+  DkdvStager<D, OWN> stg;
+  stg.init(wave, lane, ld, a);
 
   bf16x8 kf[D / 16], vf[D / 16];
   {
@@ -457,6 +538,11 @@ __global__ void __launch_bounds__(64 * NW)
     for (int kk = 0; kk < D / 16; ++kk) {
       kf[kk] = load_frag(Kp + (int64_t)krow * ld + kk * 16 + hl * 8);
       vf[kk] = load_frag(Vp + (int64_t)krow * ld + kk * 16 + hl * 8);
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      settle(kf[kk]);
+      settle(vf[kk]);
     }
   }
   f32x16 dv[D / 32], dk[D / 32];
@@ -470,30 +556,10 @@ __global__ void __launch_bounds__(64 * NW)
   const int qb0 = causal ? k0 / RB : 0;
   const int nst = (nqb - qb0 + SPLIT - 1) / SPLIT;
 
+  const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int st, int slot) {
-    char *base = smem + slot * C::STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < DL; ++j) {
-      const int uu = j * NW + wave;
-      if (uu >= SPLIT * PB) {  // padding unit: keeps the per-wave DMA count fixed
-        dma16(zero_page(), reinterpret_cast<bf16_t *>(base + SPLIT * C::BLOCK_BYTES));
-        continue;
-      }
-      const int g = uu / PB, v = uu % PB;
-      const int row0 = (qb0 + st * SPLIT + g) * RB;
-      char *blk = base + g * C::BLOCK_BYTES;
-      if (v < B::UNITS) {
-        dma_block_unit<D>(Qp, ld, row0, s, v, voff[j], reinterpret_cast<bf16_t *>(blk + v * 1024), lane);
-      } else if (v < 2 * B::UNITS) {
-        const int u = v - B::UNITS;
-        dma_block_unit<D>(dOp, a, row0, s, u, voff[j], reinterpret_cast<bf16_t *>(blk + B::BYTES + u * 1024),
-                          lane);
-      } else {  // lanes 0-7: lse of the block's 32 queries, lanes 8-15: delta (rows padded to s_pad)
-        const int i = lane & 15, r = min(row0, s_pad - RB) + 4 * (i & 7);
-        const float *src = (i < 8 ? lp : dlp) + r;
-        dma16(reinterpret_cast<const bf16_t *>(src), reinterpret_cast<bf16_t *>(blk + 2 * B::BYTES));
-      }
-    }
+    stg.issue(Qp, dOp, lp, dlp, ld, a, s, s_pad, (qb0 + st * SPLIT) * RB, smem_lds + slot * C::STAGE_BYTES,
+              wave, lane);
   };
   auto compute = [&](int st, int slot) {
     const int qb = qb0 + st * SPLIT + sp, qs0 = qb * RB;
@@ -580,13 +646,8 @@ __global__ void __launch_bounds__(64 * NW)
   const bf16_t *Kp = Qp + a;
   const bf16_t *dOp = dout + (int64_t)b * s * a + h * D;
 
-  uint32_t voff[DL];
-#pragma unroll
-  for (int j = 0; j < DL; ++j) {
-    int r, cb;
-    B::unit_src((j * NW + wave) % B::UNITS, lane, r, cb);
-    voff[j] = (uint32_t)(r * ld * 2 + cb);  // the V column offset is in the base pointer
-  }
+  KvStager<D, OWN> stg;
+  stg.init(wave, lane, ld, a);
 
   bf16x8 qf[D / 16], df[D / 16];
   const int qrow = min(qi, s - 1);
@@ -598,6 +659,13 @@ __global__ void __launch_bounds__(64 * NW)
   const bool q_ok = qi < s;
   const float lse2 = q_ok ? lse[(int64_t)bh * s_pad + qi] * LOG2E : 0.f;
   const float dlt = q_ok ? delta[(int64_t)bh * s_pad + qi] : 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    settle(qf[kk]);
+    settle(df[kk]);
+  }
+  settle(lse2);
+  settle(dlt);
   f32x16 dq[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) zero(dq[t]);
@@ -606,15 +674,8 @@ __global__ void __launch_bounds__(64 * NW)
   const int nkb = (kend + RB - 1) / RB;
   const int nst = (nkb + SPLIT - 1) / SPLIT;
 
-  auto issue = [&](int st, int slot) {
-    char *base = smem + slot * C::STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < DL; ++j) {
-      const int uu = j * NW + wave, g = uu / (2 * B::UNITS), which = (uu / B::UNITS) & 1, u = uu % B::UNITS;
-      bf16_t *dst = reinterpret_cast<bf16_t *>(base + (g * 2 + which) * B::BYTES + u * 1024);
-      dma_block_unit<D>(Kp + which * a, ld, (st * SPLIT + g) * RB, s, u, voff[j], dst, lane);
-    }
-  };
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int st, int slot) { stg.issue(Kp, ld, s, st * SPLIT * RB, smem_lds + slot * C::STAGE_BYTES); };
   auto compute = [&](int st, int slot) {
     const int kb = st * SPLIT + sp, k0 = kb * RB;
     if (kb >= nkb || (causal && k0 > qw0 + 31)) return;
