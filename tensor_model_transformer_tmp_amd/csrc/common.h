@@ -54,6 +54,33 @@ __device__ __forceinline__ void dma16(const bf16_t *src, const bf16_t *dst) {
                : "m0", "memory");
 }
 
+// LDS byte address of a shared-memory pointer (one address-space cast; the
+// DMA helpers below take 32-bit LDS addresses so that per-unit address
+// arithmetic stays in 32-bit scalar registers).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)p);
+}
+
+// DMA of one 1-KB unit with a scalar base and a per-lane 32-bit byte offset
+// (global_load_lds_dwordx4 v_off, s[base]): the 64 lanes' 16 bytes land
+// contiguously at LDS byte address lds.
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;  // uniform; made scalar explicitly
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sb)
+               : "m0", "memory");
+}
+// the same with a per-lane 64-bit source address
+__device__ __forceinline__ void dma16_v(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+               : "m0", "memory");
+}
+
 // Chunk swizzle of a row-major bf16 tile read with ds_read_b64_tr_b16: a read
 // covers 4 consecutive rows x 64 bytes per 32 lanes.  16-byte chunk c of row
 // k is stored at c ^ mc_swz(k) so those rows land in distinct 64-byte

@@ -43,22 +43,42 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 // ---- operand loaders ------------------------------------------------------
 //
 // Every operand tile goes HBM -> LDS by DMA, one 1-KB wave instruction at a
-// time.  Lanes whose source lies outside the matrix (row past the end, or k
-// past K) read a zero page instead, so partial tiles and k tails are exact.
+// time.  A loader precomputes each lane's byte offset from the tile's origin
+// once per workgroup, so a k step issues all of a wave's units from one
+// scalar base.  Rows (KC) or columns (MC) past the end of the matrix are
+// clamped to the last one: they only feed rows / columns of C that are never
+// stored.  A k tile reaching past K reads the zero page for k >= K, so
+// partial k tiles are exact.
 
 // KC tile: [ROWS][64] (k contiguous), chunk c of row r stored at c ^ swz_key(r).
 template <int ROWS, int NW>
 struct KcTile {
   static constexpr int PER_WAVE = ROWS / 8 / NW;  // DMA instructions per wave per stage
-  __device__ __forceinline__ static void issue(const bf16_t *p, int ld, int row0, int rows_total,
-                                               int k0, int K, bf16_t *tile, int wave, int lane) {
+  uint32_t voff[PER_WAVE];  // lane byte offset from element (row0, k0) of the operand
+  __device__ __forceinline__ void init(int ld, int row0, int rows_total, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int blk = j * NW + wave;               // 8-row block of the tile
       const int r = blk * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz_key<1>(r);    // global chunk landing at LDS chunk lane & 7
-      const bool ok = row0 + r < rows_total && k0 + c * 8 < K;
-      dma16(ok ? p + (int64_t)(row0 + r) * ld + k0 + c * 8 : zero_page(), tile + blk * 8 * BK);
+      const int row = min(row0 + r, rows_total - 1);
+      voff[j] = (uint32_t)(((row - row0) * ld + c * 8) * 2);
+    }
+  }
+  // tile: LDS byte address of the stage's tile
+  __device__ __forceinline__ void issue(const bf16_t *p, int ld, int row0, int k0, int K, uint32_t tile,
+                                        int wave, int lane) const {
+    const bf16_t *base = p + (int64_t)row0 * ld + k0;
+    if (k0 + BK <= K) {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) dma16_s(base, voff[j], tile + (j * NW + wave) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int r = (j * NW + wave) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz_key<1>(r);
+        dma16_v(k0 + c * 8 < K ? base + voff[j] / 2 : zero_page(), tile + (j * NW + wave) * 1024);
+      }
     }
   }
   // MFMA fragment: 8 consecutive k (half hl of substep ks) of tile row `row`
@@ -78,16 +98,30 @@ template <int ROWS, int NW>
 struct McTile {
   static constexpr int PER_WAVE = ROWS / 8 / NW;
   static constexpr int ROW_BYTES = ROWS * 2;
-  __device__ __forceinline__ static void issue(const bf16_t *p, int ld, int col0, int cols_total,
-                                               int k0, int K, bf16_t *tile, int wave, int lane) {
+  uint32_t voff[PER_WAVE];  // lane byte offset from element (k0, col0) of the operand
+  __device__ __forceinline__ static int unit_k(int blk, int lane) { return (blk * 1024 + lane * 16) / ROW_BYTES; }
+  __device__ __forceinline__ void init(int ld, int col0, int cols_total, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int blk = j * NW + wave;               // 1-KB block of the tile
       const int byte = blk * 1024 + lane * 16;
       const int kr = byte / ROW_BYTES, cp = (byte % ROW_BYTES) >> 4;
       const int c = cp ^ mc_swz<ROWS>(kr);
-      const bool ok = k0 + kr < K && col0 + c * 8 < cols_total;
-      dma16(ok ? p + (int64_t)(k0 + kr) * ld + col0 + c * 8 : zero_page(), tile + blk * 512);
+      const int col = min(col0 + c * 8, cols_total - 8);  // cols_total is a multiple of 8
+      voff[j] = (uint32_t)((kr * ld + (col - col0)) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16_t *p, int ld, int col0, int k0, int K, uint32_t tile,
+                                        int wave, int lane) const {
+    const bf16_t *base = p + (int64_t)k0 * ld + col0;
+    if (k0 + BK <= K) {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) dma16_s(base, voff[j], tile + (j * NW + wave) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j)
+        dma16_v(k0 + unit_k(j * NW + wave, lane) < K ? base + voff[j] / 2 : zero_page(),
+                tile + (j * NW + wave) * 1024);
     }
   }
   __device__ __forceinline__ static bf16x8 frag(const bf16_t *tile, int row, int ks, int hl) {
@@ -223,9 +257,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
     else if constexpr (decltype(I)::value == 1) return sB1;
     else return sB2;
   };
+  TA ta;
+  TB tb;
+  ta.init(g.lda, m0, g.M, wave, lane);
+  tb.init(g.ldb, n0, g.N, wave, lane);
   auto issue = [&](auto I, int stage) {
-    TA::issue(A, g.lda, m0, g.M, stage * BK, g.K, slotA(I), wave, lane);
-    TB::issue(B, g.ldb, n0, g.N, stage * BK, g.K, slotB(I), wave, lane);
+    ta.issue(A, g.lda, m0, stage * BK, g.K, lds_addr(slotA(I)), wave, lane);
+    tb.issue(B, g.ldb, n0, stage * BK, g.K, lds_addr(slotB(I)), wave, lane);
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
@@ -343,11 +381,13 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     // alone gives a tile per CU, 128x256 (8 waves) near that; 128x128 tiles
     // (3 stages for long k loops, 2 stages for short) while they still give
     // a tile per CU, and below that 64x128 tiles (128x64 for a weight
-    // gradient wider than it is tall)
+    // gradient wider than it is tall).  Large weight gradients wider than
+    // they are tall run best on 2-stage 128x128 tiles.
     const int64_t t256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
     const int64_t t128x256 = (int64_t)((g.M + 127) / 128) * ((g.N + 255) / 256);
     const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
-    if (t256 >= 256) v = 9;
+    if (LA == MC && g.M < g.N && t128 >= 1024) v = 5;  // wide weight gradients
+    else if (t256 >= 256) v = 9;
     else if (t128x256 >= 192) v = 8;
     else if (t128 < 256) v = LA == MC && g.M < g.N ? 11 : 10;
     else if (g.K >= 2048) v = 2;
