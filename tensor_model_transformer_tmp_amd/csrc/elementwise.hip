@@ -23,47 +23,67 @@ __device__ __forceinline__ uint4 stream_load(const uint4 *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// UNROLL vectors per thread per iteration: their UNROLL * w loads are all in
-// flight before the first add, so a small grid still keeps HBM busy.
-constexpr int SUM_UNROLL = 4;
+// two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 
+// NP peers (compile time) and UNROLL vectors per thread per iteration: all
+// UNROLL * (NP + 1) loads of an iteration are issued before the first add,
+// so a grid of a few workgroups per CU keeps enough bytes in flight for HBM.
+template <int NP>
 __global__ void __launch_bounds__(SUM_NT)
     allreduce_bf16_kernel(const uint4 *__restrict__ own, const bf16_t *__restrict__ peers,
-                          int64_t peer_stride, int n_peers, uint4 *__restrict__ out, int64_t nvec) {
+                          int64_t peer_stride, uint4 *__restrict__ out, int64_t nvec) {
+  constexpr int UNROLL = NP >= 4 ? 2 : 4;
   const int64_t stride = (int64_t)gridDim.x * SUM_NT;
-  for (int64_t v0 = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v0 < nvec; v0 += stride * SUM_UNROLL) {
-    float acc[SUM_UNROLL][8];
+  for (int64_t v0 = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v0 < nvec; v0 += stride * UNROLL) {
+    uint4 x[NP + 1][UNROLL];
 #pragma unroll
-    for (int u = 0; u < SUM_UNROLL; ++u) {
-      const int64_t v = v0 + u * stride;
-      if (v >= nvec) continue;
-      const uint4 a = stream_load(own + v);
-      acc[u][0] = lo_f32(a.x); acc[u][1] = hi_f32(a.x); acc[u][2] = lo_f32(a.y); acc[u][3] = hi_f32(a.y);
-      acc[u][4] = lo_f32(a.z); acc[u][5] = hi_f32(a.z); acc[u][6] = lo_f32(a.w); acc[u][7] = hi_f32(a.w);
-    }
-    for (int k = 0; k < n_peers; ++k) {
-      const uint4 *pk = reinterpret_cast<const uint4 *>(peers + (int64_t)k * peer_stride);
-      uint4 b[SUM_UNROLL];
+    for (int k = 0; k <= NP; ++k) {
+      const uint4 *src = k == 0 ? own : reinterpret_cast<const uint4 *>(peers + (int64_t)(k - 1) * peer_stride);
 #pragma unroll
-      for (int u = 0; u < SUM_UNROLL; ++u) {
+      for (int u = 0; u < UNROLL; ++u) {
         const int64_t v = v0 + u * stride;
-        b[u] = v < nvec ? stream_load(pk + v) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < SUM_UNROLL; ++u) {
-        acc[u][0] += lo_f32(b[u].x); acc[u][1] += hi_f32(b[u].x);
-        acc[u][2] += lo_f32(b[u].y); acc[u][3] += hi_f32(b[u].y);
-        acc[u][4] += lo_f32(b[u].z); acc[u][5] += hi_f32(b[u].z);
-        acc[u][6] += lo_f32(b[u].w); acc[u][7] += hi_f32(b[u].w);
+        x[k][u] = v < nvec ? stream_load(src + v) : make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int u = 0; u < SUM_UNROLL; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t v = v0 + u * stride;
       if (v >= nvec) continue;
-      out[v] = make_uint4(pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
-                          pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7]));
+      float acc[8] = {lo_f32(x[0][u].x), hi_f32(x[0][u].x), lo_f32(x[0][u].y), hi_f32(x[0][u].y),
+                      lo_f32(x[0][u].z), hi_f32(x[0][u].z), lo_f32(x[0][u].w), hi_f32(x[0][u].w)};
+#pragma unroll
+      for (int k = 1; k <= NP; ++k) {
+        const uint4 b = x[k][u];
+        acc[0] += lo_f32(b.x); acc[1] += hi_f32(b.x); acc[2] += lo_f32(b.y); acc[3] += hi_f32(b.y);
+        acc[4] += lo_f32(b.z); acc[5] += hi_f32(b.z); acc[6] += lo_f32(b.w); acc[7] += hi_f32(b.w);
+      }
+      out[v] = make_uint4(cvt_pk(acc[0], acc[1]), cvt_pk(acc[2], acc[3]), cvt_pk(acc[4], acc[5]),
+                          cvt_pk(acc[6], acc[7]));
     }
+  }
+}
+
+// more peers than the unrolled kernels cover: a runtime loop over the peers
+__global__ void __launch_bounds__(SUM_NT)
+    allreduce_bf16_many_kernel(const uint4 *__restrict__ own, const bf16_t *__restrict__ peers,
+                               int64_t peer_stride, int n_peers, uint4 *__restrict__ out, int64_t nvec) {
+  for (int64_t v = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * SUM_NT) {
+    const uint4 a = stream_load(own + v);
+    float acc[8] = {lo_f32(a.x), hi_f32(a.x), lo_f32(a.y), hi_f32(a.y),
+                    lo_f32(a.z), hi_f32(a.z), lo_f32(a.w), hi_f32(a.w)};
+    for (int k = 0; k < n_peers; ++k) {
+      const uint4 b = stream_load(reinterpret_cast<const uint4 *>(peers + (int64_t)k * peer_stride) + v);
+      acc[0] += lo_f32(b.x); acc[1] += hi_f32(b.x); acc[2] += lo_f32(b.y); acc[3] += hi_f32(b.y);
+      acc[4] += lo_f32(b.z); acc[5] += hi_f32(b.z); acc[6] += lo_f32(b.w); acc[7] += hi_f32(b.w);
+    }
+    out[v] = make_uint4(cvt_pk(acc[0], acc[1]), cvt_pk(acc[2], acc[3]), cvt_pk(acc[4], acc[5]),
+                        cvt_pk(acc[6], acc[7]));
   }
 }
 
@@ -158,17 +178,27 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
   if (n <= 0) return hipSuccess;
   const int64_t per_vec = bf16 ? 8 : 4;
   const int64_t nvec = n / per_vec;
-  const int64_t want = (nvec + SUM_NT * SUM_UNROLL - 1) / (SUM_NT * SUM_UNROLL);
-  const int grid = (int)(want < g_sum_grid_cap ? want : g_sum_grid_cap);
-  if (bf16)
-    OASES_LAUNCH(allreduce_bf16_kernel, dim3(grid), dim3(SUM_NT), s,
-                       static_cast<const uint4 *>(own), static_cast<const bf16_t *>(peers),
-                       peer_stride, n_peers, static_cast<uint4 *>(out), nvec);
-  else
-    OASES_LAUNCH(allreduce_f32_kernel, dim3(grid), dim3(SUM_NT), s,
-                       static_cast<const float4 *>(own), static_cast<const float *>(peers),
-                       peer_stride, n_peers, static_cast<float4 *>(out), nvec);
-  return hipGetLastError();
+  const int unroll = bf16 && n_peers <= 7 ? (n_peers >= 4 ? 2 : 4) : 1;
+  const int64_t want = (nvec + (int64_t)SUM_NT * unroll - 1) / ((int64_t)SUM_NT * unroll);
+  const dim3 grid((unsigned)(want < g_sum_grid_cap ? want : g_sum_grid_cap));
+  const uint4 *o = static_cast<const uint4 *>(own);
+  const bf16_t *p = static_cast<const bf16_t *>(peers);
+  uint4 *y = static_cast<uint4 *>(out);
+  if (!bf16) {
+    OASES_LAUNCH(allreduce_f32_kernel, grid, dim3(SUM_NT), s, static_cast<const float4 *>(own),
+                 static_cast<const float *>(peers), peer_stride, n_peers, static_cast<float4 *>(out), nvec);
+    return hipSuccess;
+  }
+  switch (n_peers) {
+#define OASES_SUM_CASE(NP) \
+  case NP: OASES_LAUNCH(allreduce_bf16_kernel<NP>, grid, dim3(SUM_NT), s, o, p, peer_stride, y, nvec); break;
+    OASES_SUM_CASE(0) OASES_SUM_CASE(1) OASES_SUM_CASE(2) OASES_SUM_CASE(3)
+    OASES_SUM_CASE(4) OASES_SUM_CASE(5) OASES_SUM_CASE(6) OASES_SUM_CASE(7)
+#undef OASES_SUM_CASE
+    default:
+      OASES_LAUNCH(allreduce_bf16_many_kernel, grid, dim3(SUM_NT), s, o, p, peer_stride, n_peers, y, nvec);
+  }
+  return hipSuccess;
 }
 
 void allreduce_set_grid_cap(int cap) { g_sum_grid_cap = cap; }
