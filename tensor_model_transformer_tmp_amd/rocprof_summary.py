@@ -11,6 +11,8 @@ trace and a counter run can be set beside the event timings.
   python -m tensor_model_transformer_tmp_amd.rocprof_summary traffic --kernel K \
       --fetch <counter_collection.csv> --write <counter_collection.csv> \
       --calib-fetch <csv> --calib-write <csv> --calib-bytes N
+  python -m tensor_model_transformer_tmp_amd.rocprof_summary traffic-all --workload W \
+      --outdir profiles ... (same inputs; one <class>_<W>_traffic.txt per class)
 
 ``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
 same counters read for a plain copy of known size (the sum kernel with no
@@ -32,7 +34,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 # kernels whose launch count is the class launch count (the other kernels of a
 # multi-kernel class add their time to it)
-_LEAD = {"attn_bwd": "attn_bwd_dkdv", "colsum": "colsum_pass1"}
+_LEAD = {"attn_bwd": "attn_dkdv", "colsum": "colsum_pass1"}
 
 SOURCES = {
     "gemm_fwd": ("gemm_bf16.hip", "gemm_f32.hip"),
@@ -75,9 +77,8 @@ def kernel_class(name: str):
     m = _GEMM.search(name)
     if m:
         return {("0", "0"): "gemm_fwd", ("0", "1"): "gemm_dx", ("1", "1"): "gemm_dw"}.get(m.groups())
-    for key, cls in (("attn_fwd", "attn_fwd"), ("attn_bwd_dkdv", "attn_bwd"),
-                     ("attn_bwd_dq", "attn_bwd"), ("attn_delta", "attn_bwd"),
-                     ("allreduce_", "sum"), ("colsum_pass", "colsum")):
+    for key, cls in (("attn_fwd", "attn_fwd"), ("attn_dkdv", "attn_bwd"), ("attn_dq", "attn_bwd"),
+                     ("attn_delta", "attn_bwd"), ("allreduce_", "sum"), ("colsum_pass", "colsum")):
         if key in name:
             return cls
     return None
@@ -99,7 +100,8 @@ def stats_table(path: str) -> str:
         n = names[r["Name"]]
         cls = kernel_class(n)
         calls, tot = int(r["Calls"]), float(r["TotalDurationNs"])
-        short = re.sub(r"\(.*$", "", n.replace("oases::", "").replace("(anonymous namespace)::", ""))
+        short = n.replace("(anonymous namespace)::", "").replace("(oases::Layout)", "L").replace("oases::", "")
+        short = re.sub(r"^void ", "", re.sub(r"\(.*$", "", short))
         out.append(f"{short[:90]} | {calls} | {tot / 1e3:.1f} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {cls or '-'}")
         if cls:
@@ -130,34 +132,58 @@ def pmc_per_class(path: str, counter: str):
     return {c: (launches[c], tot[c] / max(launches[c], 1)) for c in tot}
 
 
+def traffic_lines(kernel, fetch_csv, write_csv, cf_csv, cw_csv, calib_bytes):
+    fetch = pmc_per_class(fetch_csv, "FETCH_SIZE").get(kernel)
+    write = pmc_per_class(write_csv, "WRITE_SIZE").get(kernel)
+    if fetch is None or write is None:
+        return None
+    cf = pmc_per_class(cf_csv, "FETCH_SIZE")["sum"]
+    cw = pmc_per_class(cw_csv, "WRITE_SIZE")["sum"]
+    kf, kw = calib_bytes / cf[1], calib_bytes / cw[1]
+    return [f"copy calibration: {calib_bytes:.0f} B read and written per launch of the sum kernel "
+            f"with no peers; FETCH_SIZE {cf[1]:.1f} -> {kf:.2f} B per unit; "
+            f"WRITE_SIZE {cw[1]:.1f} -> {kw:.2f} B per unit",
+            f"kernel class: {kernel} ({fetch[0]} launches in the FETCH_SIZE run, "
+            f"{write[0]} in the WRITE_SIZE run)",
+            f"fetch_bytes_per_launch: {fetch[1] * kf:.0f}",
+            f"write_bytes_per_launch: {write[1] * kw:.0f}",
+            f"sources_sha256: {sources_hash(kernel)}"]
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
-    t = sub.add_parser("traffic")
-    t.add_argument("--kernel", required=True, choices=sorted(SOURCES))
-    t.add_argument("--fetch", required=True)
-    t.add_argument("--write", required=True)
-    t.add_argument("--calib-fetch", required=True)
-    t.add_argument("--calib-write", required=True)
-    t.add_argument("--calib-bytes", type=float, required=True)
+    for name in ("traffic", "traffic-all"):
+        t = sub.add_parser(name)
+        if name == "traffic":
+            t.add_argument("--kernel", required=True, choices=sorted(SOURCES))
+        else:
+            t.add_argument("--workload", required=True)
+            t.add_argument("--outdir", required=True)
+            t.add_argument("--header", default="", help="text placed before the figures")
+        t.add_argument("--fetch", required=True)
+        t.add_argument("--write", required=True)
+        t.add_argument("--calib-fetch", required=True)
+        t.add_argument("--calib-write", required=True)
+        t.add_argument("--calib-bytes", type=float, required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv))
         return 0
-    fetch = pmc_per_class(a.fetch, "FETCH_SIZE")[a.kernel]
-    write = pmc_per_class(a.write, "WRITE_SIZE")[a.kernel]
-    cf = pmc_per_class(a.calib_fetch, "FETCH_SIZE")["sum"]
-    cw = pmc_per_class(a.calib_write, "WRITE_SIZE")["sum"]
-    kf, kw = a.calib_bytes / cf[1], a.calib_bytes / cw[1]
-    print(f"copy calibration: {a.calib_bytes:.0f} B read and written per launch; "
-          f"FETCH_SIZE {cf[1]:.1f} KiB -> factor {kf:.2f} B per unit; "
-          f"WRITE_SIZE {cw[1]:.1f} KiB -> factor {kw:.2f} B per unit")
-    print(f"kernel class: {a.kernel} ({fetch[0]} launches in the fetch run, {write[0]} in the write run)")
-    print(f"fetch_bytes_per_launch: {fetch[1] * kf:.0f}")
-    print(f"write_bytes_per_launch: {write[1] * kw:.0f}")
-    print(f"sources_sha256: {sources_hash(a.kernel)}")
+    args = (a.fetch, a.write, a.calib_fetch, a.calib_write, a.calib_bytes)
+    if a.cmd == "traffic":
+        print("\n".join(traffic_lines(a.kernel, *args)))
+        return 0
+    for kernel in sorted(SOURCES):
+        lines = traffic_lines(kernel, *args)
+        if lines is None:
+            continue
+        path = os.path.join(a.outdir, f"{kernel}_{a.workload}_traffic.txt")
+        with open(path, "w") as fh:
+            fh.write(a.header + "\n".join(lines) + "\n")
+        print("wrote", path)
     return 0
 
 
