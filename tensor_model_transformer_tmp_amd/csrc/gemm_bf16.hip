@@ -207,9 +207,29 @@ __device__ __forceinline__ void epilogue_row(const GemmArgs &g, int m, const int
 
 // ---- kernel -----------------------------------------------------------------
 
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// wait until at most n * DL of this wave's vector-memory operations are
+// outstanding, for a runtime n in [0, NMAX]
+template <int NMAX, int DL>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (NMAX <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= NMAX) wait_vmcnt<NMAX * DL>();
+    else wait_vmcnt_upto<NMAX - 1, DL>(n);
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
-  static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
+  static_assert(STAGES >= 2 && STAGES <= 6, "2 to 6 stages");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -217,12 +237,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   using TA = Tile<BM, NW, LA>;
   using TB = Tile<BN, NW, LB>;
   constexpr int DL = TA::PER_WAVE + TB::PER_WAVE;  // DMA instructions per wave per stage
-  // One LDS variable per stage and operand, selected with compile-time slot
-  // indices, so the compiler sees that the fragment reads of one stage and
-  // the DMA into another do not alias.
-  __shared__ __attribute__((aligned(1024))) bf16_t sA0[BM * BK], sA1[BM * BK];
-  __shared__ __attribute__((aligned(1024))) bf16_t sB0[BN * BK], sB1[BN * BK];
-  __shared__ __attribute__((aligned(1024))) bf16_t sA2[STAGES > 2 ? BM * BK : 8], sB2[STAGES > 2 ? BN * BK : 8];
+  static_assert((STAGES - 2) * DL < 64, "vmcnt range");
+  static_assert(STAGES * (BM + BN) * BK * 2 <= 160 * 1024, "LDS");
+  // LDS ring of STAGES slots per operand, always indexed with compile-time
+  // slot numbers (fragment reads get immediate offsets)
+  __shared__ __attribute__((aligned(1024))) bf16_t sA[STAGES][BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB[STAGES][BN * BK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,16 +267,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   const bf16_t *B = static_cast<const bf16_t *>(g.B);
   const int nk = (g.K + BK - 1) / BK;
 
-  auto slotA = [&](auto I) -> bf16_t * {
-    if constexpr (decltype(I)::value == 0) return sA0;
-    else if constexpr (decltype(I)::value == 1) return sA1;
-    else return sA2;
-  };
-  auto slotB = [&](auto I) -> bf16_t * {
-    if constexpr (decltype(I)::value == 0) return sB0;
-    else if constexpr (decltype(I)::value == 1) return sB1;
-    else return sB2;
-  };
+  auto slotA = [&](auto I) -> bf16_t * { return sA[decltype(I)::value]; };
+  auto slotB = [&](auto I) -> bf16_t * { return sB[decltype(I)::value]; };
   TA ta;
   TB tb;
   ta.init(g.lda, m0, g.M, wave, lane);
@@ -265,10 +277,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
     ta.issue(A, g.lda, m0, stage * BK, g.K, lds_addr(slotA(I)), wave, lane);
     tb.issue(B, g.ldb, n0, stage * BK, g.K, lds_addr(slotB(I)), wave, lane);
   };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-
   f32x16 acc[TN][TM];
 #pragma unroll
   for (int j = 0; j < TN; ++j)
@@ -278,16 +286,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
   // prologue: stages 0 .. STAGES-2 in flight
-  issue(C0{}, 0);
-  if constexpr (STAGES == 3)
-    if (nk > 1) issue(C1{}, 1);
+  static_for<0, STAGES - 1>([&](auto I) {
+    if (decltype(I)::value < nk) issue(I, decltype(I)::value);
+  });
 
   // one k tile in LDS slot I (static); stage kt+STAGES-1 goes to slot I+STAGES-1
   auto step = [&](auto I, int kt) {
     using AHEAD = std::integral_constant<int, (decltype(I)::value + STAGES - 1) % STAGES>;
-    // this stage's DMA is done once at most the later stage's DMA is outstanding
-    if (STAGES == 3 && kt + 1 < nk) wait_vmcnt<DL>();
-    else wait_vmcnt<0>();
+    // this stage's DMA is done once at most the later stages' DMA is outstanding
+    wait_vmcnt_upto<STAGES - 2, DL>(min(STAGES - 2, nk - 1 - kt));
     lds_barrier();
     if (kt + STAGES - 1 < nk) issue(AHEAD{}, kt + STAGES - 1);
 
@@ -332,14 +339,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
 
   // full groups of STAGES k tiles (slots 0..STAGES-1 in order), then the tail
   int kt = 0;
-  for (; kt + STAGES <= nk; kt += STAGES) {
-    step(C0{}, kt);
-    step(C1{}, kt + 1);
-    if constexpr (STAGES == 3) step(C2{}, kt + 2);
-  }
-  if (kt < nk) step(C0{}, kt);
-  if constexpr (STAGES == 3)
-    if (kt + 1 < nk) step(C1{}, kt + 1);
+  for (; kt + STAGES <= nk; kt += STAGES) static_for<0, STAGES>([&](auto I) { step(I, kt + decltype(I)::value); });
+  static_for<0, STAGES - 1>([&](auto I) {
+    if (kt + decltype(I)::value < nk) step(I, kt + decltype(I)::value);
+  });
 
   // epilogue: acc[j][i][jj*4 + ii] is C[m][n] with
   //   m = m0 + wm*WTM + i*32 + l32,  n = n0 + wn*WTN + j*32 + jj*8 + hl*4 + ii
@@ -381,30 +384,33 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     // alone gives a tile per CU, 128x256 (8 waves) near that; 128x128 tiles
     // (3 stages for long k loops, 2 stages for short) while they still give
     // a tile per CU, and below that 64x128 tiles (128x64 for a weight
-    // gradient wider than it is tall).  Large weight gradients wider than
-    // they are tall run best on 2-stage 128x128 tiles.
+    // gradient wider than it is tall), 4 stages deep for k >= 4096.  Large
+    // weight gradients wider than they are tall run best on 2-stage 128x128.
     const int64_t t256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
     const int64_t t128x256 = (int64_t)((g.M + 127) / 128) * ((g.N + 255) / 256);
     const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
-    if (LA == MC && g.M < g.N && t128 >= 1024) v = 5;  // wide weight gradients
-    else if (t256 >= 256) v = 9;
-    else if (t128x256 >= 192) v = 8;
-    else if (t128 < 256) v = LA == MC && g.M < g.N ? 11 : 10;
+    const bool wide_dw = LA == MC && g.M < g.N;
+    if (wide_dw && t128 >= 1024) v = 5;
+    else if (t256 >= 256) v = 4;
+    else if (t128x256 >= 192) v = 3;
+    else if (t128 < 256) v = g.K >= 4096 ? (wide_dw ? 12 : 9) : (wide_dw ? 8 : 7);
     else if (g.K >= 2048) v = 2;
     else v = 5;
   }
   switch (v) {
-    case 1: return launch<256, 128, 2, 2, 3, LA, LB, EPI>(g, s);
+    case 1: return launch<256, 128, 4, 2, 3, LA, LB, EPI>(g, s);
     case 2: return launch<128, 128, 2, 2, 3, LA, LB, EPI>(g, s);
-    case 3: return launch<128, 256, 2, 2, 3, LA, LB, EPI>(g, s);
-    case 4: return launch<256, 256, 2, 2, 2, LA, LB, EPI>(g, s);
+    case 3: return launch<128, 256, 2, 4, 3, LA, LB, EPI>(g, s);
+    case 4: return launch<256, 256, 4, 2, 2, LA, LB, EPI>(g, s);
     case 5: return launch<128, 128, 2, 2, 2, LA, LB, EPI>(g, s);
-    case 6: return launch<256, 128, 4, 2, 3, LA, LB, EPI>(g, s);
-    case 7: return launch<256, 256, 2, 4, 2, LA, LB, EPI>(g, s);
-    case 8: return launch<128, 256, 2, 4, 3, LA, LB, EPI>(g, s);
-    case 9: return launch<256, 256, 4, 2, 2, LA, LB, EPI>(g, s);
-    case 10: return launch<64, 128, 2, 2, 2, LA, LB, EPI>(g, s);
-    case 11: return launch<128, 64, 2, 2, 2, LA, LB, EPI>(g, s);
+    case 6: return launch<256, 256, 2, 4, 2, LA, LB, EPI>(g, s);
+    case 7: return launch<64, 128, 2, 2, 2, LA, LB, EPI>(g, s);
+    case 8: return launch<128, 64, 2, 2, 2, LA, LB, EPI>(g, s);
+    case 9: return launch<64, 128, 2, 2, 4, LA, LB, EPI>(g, s);
+    case 10: return launch<64, 128, 2, 2, 6, LA, LB, EPI>(g, s);
+    case 11: return launch<128, 128, 2, 2, 4, LA, LB, EPI>(g, s);
+    case 12: return launch<128, 64, 2, 2, 4, LA, LB, EPI>(g, s);
+    case 13: return launch<128, 128, 4, 2, 4, LA, LB, EPI>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
