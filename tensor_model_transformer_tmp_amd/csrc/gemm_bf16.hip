@@ -28,17 +28,19 @@
 namespace oases {
 namespace {
 
-constexpr int BK = 64;          // k tile (elements)
-constexpr int ROWB = BK * 2;    // LDS bytes per tile row (unpadded, swizzled)
+// A k tile is BK = 64 or 32 elements deep (a kernel template parameter): 64
+// for the 2-3 stage pipelines, 32 to fit 4-5 stages of the largest tiles in
+// the 160 KB of LDS.
 
-
-// element offset of (row, 16-byte chunk) in a swizzled [rows][64] tile.
-// SW 0: chunk ^ (row & 7) -- distinct banks for 8 consecutive rows (32 banks);
-// SW 1: chunk ^ ((row ^ (row >> 3)) & 7) -- also distinct across 16 rows (64 banks).
-template <int SW>
-__device__ __forceinline__ int swz_key(int row) { return SW ? ((row ^ (row >> 3)) & 7) : (row & 7); }
-template <int SW>
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key<SW>(row)) << 3); }
+// KC tile row swizzle: 16-byte chunk c of row r is stored at c ^ kc_key(r).
+// 64-deep rows (128 B): (r ^ (r >> 3)) & 7 puts 16 consecutive rows' copies
+// of one chunk in distinct 16-byte bank slots; 32-deep rows (64 B, four rows
+// per 256-byte bank window): (r >> 2) & 3 does the same.
+template <int BK>
+__device__ __forceinline__ int kc_key(int row) {
+  static_assert(BK == 64 || BK == 32, "k tile depth");
+  return BK == 64 ? ((row ^ (row >> 3)) & 7) : ((row >> 2) & 3);
+}
 
 // ---- operand loaders ------------------------------------------------------
 //
@@ -50,17 +52,20 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 // stored.  A k tile reaching past K reads the zero page for k >= K, so
 // partial k tiles are exact.
 
-// KC tile: [ROWS][64] (k contiguous), chunk c of row r stored at c ^ swz_key(r).
-template <int ROWS, int NW>
+// KC tile: [ROWS][BK] (k contiguous), chunk c of row r stored at c ^ kc_key(r).
+template <int ROWS, int NW, int BK>
 struct KcTile {
-  static constexpr int PER_WAVE = ROWS / 8 / NW;  // DMA instructions per wave per stage
+  static constexpr int RPU = 512 / BK;  // rows per 1-KB DMA unit
+  static constexpr int CPR = BK / 8;    // 16-byte chunks per row
+  static_assert((ROWS / RPU) % NW == 0, "units per wave");
+  static constexpr int PER_WAVE = ROWS / RPU / NW;  // DMA instructions per wave per stage
   uint32_t voff[PER_WAVE];  // lane byte offset from element (row0, k0) of the operand
   __device__ __forceinline__ void init(int ld, int row0, int rows_total, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int blk = j * NW + wave;               // 8-row block of the tile
-      const int r = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz_key<1>(r);    // global chunk landing at LDS chunk lane & 7
+      const int blk = j * NW + wave;               // RPU-row block of the tile
+      const int r = blk * RPU + lane / CPR;
+      const int c = (lane % CPR) ^ kc_key<BK>(r);  // global chunk landing at LDS chunk lane % CPR
       const int row = min(row0 + r, rows_total - 1);
       voff[j] = (uint32_t)(((row - row0) * ld + c * 8) * 2);
     }
@@ -75,29 +80,30 @@ struct KcTile {
     } else {
 #pragma unroll
       for (int j = 0; j < PER_WAVE; ++j) {
-        const int r = (j * NW + wave) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz_key<1>(r);
+        const int r = (j * NW + wave) * RPU + lane / CPR;
+        const int c = (lane % CPR) ^ kc_key<BK>(r);
         dma16_v(k0 + c * 8 < K ? base + voff[j] / 2 : zero_page(), tile + (j * NW + wave) * 1024);
       }
     }
   }
   // MFMA fragment: 8 consecutive k (half hl of substep ks) of tile row `row`
   __device__ __forceinline__ static bf16x8 frag(const bf16_t *tile, int row, int ks, int hl) {
-    return *reinterpret_cast<const bf16x8 *>(tile + swz<1>(row, ks * 2 + hl));
+    return *reinterpret_cast<const bf16x8 *>(tile + row * BK + (((ks * 2 + hl) ^ kc_key<BK>(row)) << 3));
   }
 };
 
-// MC tile: [64 k][ROWS] (row index contiguous), 16-byte chunk c of k-row k
+// MC tile: [BK k][ROWS] (row index contiguous), 16-byte chunk c of k-row k
 // stored at c ^ mc_swz(k).  Fragments are read with the gfx950 transposing
 // LDS read: in each 16-lane group, source lane s addresses k-row k0 + s/4 at
 // columns n0 + 4 (s % 4); lane i of the group then receives k0..k0+3 of column
 // n0 + i.  Two such reads give the 8 consecutive k of a KC fragment, so both
 // tile kinds feed the same MFMA.  The swizzle spreads the 4 k-rows of a read
 // over the four 64-byte quarters of the 256-byte bank space.
-template <int ROWS, int NW>
+template <int ROWS, int NW, int BK>
 struct McTile {
-  static constexpr int PER_WAVE = ROWS / 8 / NW;
   static constexpr int ROW_BYTES = ROWS * 2;
+  static_assert((BK * ROW_BYTES / 1024) % NW == 0, "units per wave");
+  static constexpr int PER_WAVE = BK * ROW_BYTES / 1024 / NW;
   uint32_t voff[PER_WAVE];  // lane byte offset from element (k0, col0) of the operand
   __device__ __forceinline__ static int unit_k(int blk, int lane) { return (blk * 1024 + lane * 16) / ROW_BYTES; }
   __device__ __forceinline__ void init(int ld, int col0, int cols_total, int wave, int lane) {
@@ -140,8 +146,8 @@ struct McTile {
   }
 };
 
-template <int ROWS, int NW, Layout L>
-using Tile = typename std::conditional<L == KC, KcTile<ROWS, NW>, McTile<ROWS, NW>>::type;
+template <int ROWS, int NW, Layout L, int BK>
+using Tile = typename std::conditional<L == KC, KcTile<ROWS, NW, BK>, McTile<ROWS, NW, BK>>::type;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -227,15 +233,15 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, Layout LA, Layout LB, int EPI>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   static_assert(STAGES >= 2 && STAGES <= 6, "2 to 6 stages");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  static_assert(TM >= 1 && TN >= 1 && (BM / 8) % NW == 0 && (BN / 8) % NW == 0, "tile shape");
-  using TA = Tile<BM, NW, LA>;
-  using TB = Tile<BN, NW, LB>;
+  static_assert(TM >= 1 && TN >= 1, "tile shape");
+  using TA = Tile<BM, NW, LA, BK>;
+  using TB = Tile<BN, NW, LB, BK>;
   constexpr int DL = TA::PER_WAVE + TB::PER_WAVE;  // DMA instructions per wave per stage
   static_assert((STAGES - 2) * DL < 64, "vmcnt range");
   static_assert(STAGES * (BM + BN) * BK * 2 <= 160 * 1024, "LDS");
@@ -366,10 +372,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI>
+template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI, int BK = 64>
 hipError_t launch(const GemmArgs &g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  OASES_LAUNCH((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, LA, LB, EPI>), dim3(tiles),
+  OASES_LAUNCH((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, BK, LA, LB, EPI>), dim3(tiles),
                      dim3(64 * WGM * WGN), s, g);
   return hipGetLastError();
 }
@@ -384,8 +390,9 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     // alone gives a tile per CU, 128x256 (8 waves) near that; 128x128 tiles
     // (3 stages for long k loops, 2 stages for short) while they still give
     // a tile per CU, and below that 64x128 tiles (128x64 for a weight
-    // gradient wider than it is tall), 4 stages deep for k >= 4096.  Large
-    // weight gradients wider than they are tall run best on 2-stage 128x128.
+    // gradient wider than it is tall), 4 stages deep for k >= 4096 (8-wave
+    // 128x128 tiles when those nearly cover the CUs).  Large weight
+    // gradients wider than they are tall run best on 2-stage 128x128.
     const int64_t t256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
     const int64_t t128x256 = (int64_t)((g.M + 127) / 128) * ((g.N + 255) / 256);
     const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
@@ -393,7 +400,7 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     if (wide_dw && t128 >= 1024) v = 5;
     else if (t256 >= 256) v = 4;
     else if (t128x256 >= 192) v = 3;
-    else if (t128 < 256) v = g.K >= 4096 ? (wide_dw ? 12 : 9) : (wide_dw ? 8 : 7);
+    else if (t128 < 256) v = g.K >= 4096 ? (t128 >= 192 ? 13 : (wide_dw ? 12 : 9)) : (wide_dw ? 8 : 7);
     else if (g.K >= 2048) v = 2;
     else v = 5;
   }
@@ -411,6 +418,10 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     case 11: return launch<128, 128, 2, 2, 4, LA, LB, EPI>(g, s);
     case 12: return launch<128, 64, 2, 2, 4, LA, LB, EPI>(g, s);
     case 13: return launch<128, 128, 4, 2, 4, LA, LB, EPI>(g, s);
+    case 14: return launch<256, 256, 4, 2, 4, LA, LB, EPI, 32>(g, s);
+    case 15: return launch<256, 256, 4, 2, 5, LA, LB, EPI, 32>(g, s);
+    case 16: return launch<128, 256, 2, 4, 5, LA, LB, EPI, 32>(g, s);
+    case 17: return launch<256, 128, 4, 2, 5, LA, LB, EPI, 32>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
