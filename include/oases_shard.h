@@ -225,7 +225,7 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
                int32_t beta, void *stream);
 
 /* Tile configuration of the bf16 GEMMs for this process: 0 = automatic (the
- * default), 1..17 force one of the compiled tile shapes and pipeline depths
+ * default), 1..19 force one of the compiled tile shapes and pipeline depths
  * (tests and tuning sweeps).  Returns OASES_E_ARG for other values. */
 int oases_gemm_tile_variant(int32_t variant);
 

@@ -743,7 +743,7 @@ int oases_attention_variant(int32_t variant) {
 }
 
 int oases_gemm_tile_variant(int32_t variant) {
-  if (variant < 0 || variant > 17) return OASES_E_ARG;
+  if (variant < 0 || variant > 19) return OASES_E_ARG;
   gemm_bf16_set_variant(variant);
   return OASES_OK;
 }

@@ -391,16 +391,19 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     // (3 stages for long k loops, 2 stages for short) while they still give
     // a tile per CU, and below that 64x128 tiles (128x64 for a weight
     // gradient wider than it is tall), 4 stages deep for k >= 4096 (8-wave
-    // 128x128 tiles when those nearly cover the CUs).  Large weight
+    // 128x128 tiles when those nearly cover the CUs); short-k problems that
+    // 64x64 tiles cover in at most two rounds run on those.  Large weight
     // gradients wider than they are tall run best on 2-stage 128x128.
     const int64_t t256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
     const int64_t t128x256 = (int64_t)((g.M + 127) / 128) * ((g.N + 255) / 256);
     const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
+    const int64_t t64 = (int64_t)((g.M + 63) / 64) * ((g.N + 63) / 64);
     const bool wide_dw = LA == MC && g.M < g.N;
     if (wide_dw && t128 >= 1024) v = 5;
     else if (t256 >= 256) v = 4;
     else if (t128x256 >= 192) v = 3;
-    else if (t128 < 256) v = g.K >= 4096 ? (t128 >= 192 ? 13 : (wide_dw ? 12 : 9)) : (wide_dw ? 8 : 7);
+    else if (t128 < 256 && g.K >= 4096) v = t128 >= 192 ? 13 : (wide_dw ? 12 : 9);
+    else if (t128 < 256) v = t64 <= 512 ? (wide_dw ? 19 : 18) : (wide_dw ? 8 : 7);
     else if (g.K >= 2048) v = 2;
     else v = 5;
   }
@@ -422,6 +425,8 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     case 15: return launch<256, 256, 4, 2, 5, LA, LB, EPI, 32>(g, s);
     case 16: return launch<128, 256, 2, 4, 5, LA, LB, EPI, 32>(g, s);
     case 17: return launch<256, 128, 4, 2, 5, LA, LB, EPI, 32>(g, s);
+    case 18: return launch<64, 64, 2, 2, 2, LA, LB, EPI>(g, s);
+    case 19: return launch<64, 64, 2, 2, 4, LA, LB, EPI>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
