@@ -2,12 +2,16 @@
 
 A step is one pass of the whole hot path over one micro-batch of seeded
 synthetic input: forward of every block for both sub-batches with the
-AllReduce-point sums on the side stream, then the fine-grained recompute and
-backward of every block (Oases overlapped schedule), replayed as one hipGraph.
+AllReduce-point sums overlapping the other sub-batch's compute, then the
+fine-grained recompute and backward of every block (Oases overlapped
+schedule).  The overlap is realised either with a side stream and events or
+by running each sum on extra workgroups of the next GEMM launch; each
+eagerly or as one hipGraph.  The fastest of the four is timed.
 
 Prints one JSON line.  ``value`` is the counted (algorithmic) TFLOP/s of the
-step; the roofline entry is for the dominant kernel, timed with HIP events on
-its own stream; the CPU baseline is the float64 oracle on this host's cores.
+step; the roofline entry is for the kernel class with the most time per
+step, timed with HIP events carried in its kernels' dispatch packets; the
+CPU baseline is the float64 oracle on this host's cores.
 """
 from __future__ import annotations
 
@@ -179,7 +183,7 @@ def main():
 
     cfg = gen.PRESETS[args.config]
     inp = gen.make_inputs(cfg)
-    dev = DeviceShard(inp, device="cuda:0", modes=("overlap_fine", "serial_fine"))
+    dev = DeviceShard(inp, device="cuda:0", modes=("overlap_fine", "overlap_fused", "serial_fine"))
     del inp
 
     def run(mode, graph, n):
@@ -194,14 +198,18 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
-    # The overlapped fine-grained schedule is issued either eagerly on the two
-    # streams or as one captured hipGraph per step; both are timed briefly and
-    # the faster one is the timed region.  The same kernels serialised on one
-    # stream give the reference for the hidden-reduction estimate.
+    # The overlapped fine-grained schedule has two realisations: the sums on
+    # a side stream ordered with events (overlap_fine), or the sums as extra
+    # workgroups of the next GEMM launch on the compute stream
+    # (overlap_fused).  Each is issued eagerly or replayed as one hipGraph;
+    # all four are probed briefly and the fastest is the timed region.  The
+    # same kernels serialised on one stream give the reference for the
+    # hidden-reduction estimate.
     probe = max(3, args.steps // 5)
-    launch = {g: timed("overlap_fine", g, probe, 2) for g in (False, True)}
-    use_graph = launch[True] <= launch[False]
-    sec = timed("overlap_fine", use_graph, args.steps, args.warmup)
+    launch = {(m, g): timed(m, g, probe, 2) for m in ("overlap_fine", "overlap_fused")
+              for g in (False, True)}
+    mode, use_graph = min(launch, key=launch.get)
+    sec = timed(mode, use_graph, args.steps, args.warmup)
     sec_serial = timed("serial_fine", use_graph, max(5, args.steps // 2), 3)
 
     # Per-kernel-class timing: eager overlapped steps with a pair of HIP events
@@ -259,12 +267,12 @@ def main():
                    "micro_batch": cfg.micro_batch, "seq_len": cfg.seq, "hidden": cfg.hidden,
                    "heads_per_shard": cfg.heads_per_shard, "head_dim": cfg.head_dim,
                    "ffn_shard": cfg.ffn_shard, "tmp_width": cfg.tmp_width,
-                   "schedule": "overlap_fine+" + ("hipGraph" if use_graph else "eager-2-streams"),
+                   "schedule": mode + "+" + ("hipGraph" if use_graph else "eager"),
                    "parallelism": "one TMP shard, 1 GPU"},
         "mfma_peak_frac": value / MFMA_BF16_PEAK_TFLOPS,
         "reduction_hidden_frac": hidden,
         "serial_ms_per_step": sec_serial * 1e3,
-        "launch_probe_ms": {"eager": launch[False] * 1e3, "graph": launch[True] * 1e3},
+        "launch_probe_ms": {f"{m}+{'graph' if g else 'eager'}": t * 1e3 for (m, g), t in launch.items()},
         "sum_ms_per_step": sum_per_step * 1e3,
         "kernels": kernels,
         "gflop_per_step": {"fwd": f / 1e9, "recompute": r / 1e9, "bwd": b / 1e9},

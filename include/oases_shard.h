@@ -73,15 +73,22 @@ typedef enum { OASES_ATTN = 0, OASES_FFN = 1 } oases_block;
 
 /* Step schedules (Section IV, Fig. 4).  OVERLAP_FINE issues every AllReduce
  * point on the side stream so that one sub-batch's sum overlaps the other
- * sub-batch's compute; the SERIAL modes issue everything on the compute
- * stream.  DEFAULT_RECOMPUTE recomputes the whole block including its row
- * GEMM and issues C(R) (its result is discarded); NO_RECOMPUTE keeps every
- * block's intermediates from the forward pass (needs a larger workspace). */
+ * sub-batch's compute, ordered with events; OVERLAP_FUSED (same op list)
+ * runs each AllReduce point on extra workgroups of the next GEMM launched on
+ * the compute stream -- the other sub-batch's GEMM, or the dW GEMM of the
+ * backward -- so the two run concurrently without cross-queue events
+ * (float32 configurations issue the sum as its own kernel on the compute
+ * stream).  The SERIAL modes issue everything on the compute stream.
+ * DEFAULT_RECOMPUTE recomputes the whole block including its row GEMM and
+ * issues C(R) (its result is discarded); NO_RECOMPUTE keeps every block's
+ * intermediates from the forward pass (needs a larger workspace).  All modes
+ * give bit-identical results. */
 typedef enum {
   OASES_OVERLAP_FINE = 0,
   OASES_SERIAL_FINE = 1,
   OASES_SERIAL_DEFAULT_RECOMPUTE = 2,
-  OASES_SERIAL_NO_RECOMPUTE = 3
+  OASES_SERIAL_NO_RECOMPUTE = 3,
+  OASES_OVERLAP_FUSED = 4
 } oases_mode;
 
 /* Shape of the shard.  Constraints (OASES_E_SHAPE otherwise):
@@ -230,8 +237,10 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
 int oases_gemm_tile_variant(int32_t variant);
 
 /* Largest number of workgroups of the AllReduce-point sum kernel for this
- * process (default 512).  A smaller grid leaves CUs to the other stream's
- * compute while a sum runs beside it.  1..65536, else OASES_E_ARG. */
+ * process (default 512); a sum fused into a GEMM launch (OVERLAP_FUSED)
+ * uses at most half as many.  A smaller grid leaves CUs to the compute that
+ * runs beside a sum.  Graphs already captured keep the value they were
+ * captured with.  1..65536, else OASES_E_ARG. */
 int oases_sum_grid_cap(int32_t workgroups);
 
 /* Attention work split for this process.  A workgroup has 4 waves of 32

@@ -203,6 +203,15 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
 
 void allreduce_set_grid_cap(int cap) { g_sum_grid_cap = cap; }
 
+int allreduce_fused_wgs(int64_t nvec) {
+  // half the standalone grid cap: beside a GEMM's tiles, a larger sum grid
+  // takes CUs the GEMM needs (measured best at 128-256 workgroups)
+  const int64_t want = (nvec + 256 * 2 - 1) / (256 * 2);
+  const int64_t cap = g_sum_grid_cap < 16 ? 8 : g_sum_grid_cap / 2;
+  const int64_t w = want < cap ? want : cap;
+  return (int)((w + 7) / 8 * 8);
+}
+
 int64_t colsum_partial_floats(int rows, int cols) {
   return (int64_t)((rows + CS_ROWS - 1) / CS_ROWS) * cols;
 }

@@ -154,7 +154,7 @@ int check_config(const oases_config *cfg, Dims *D, std::string *err) {
 
 std::vector<Op> build_ops(int L, int mode) {
   std::vector<Op> ops;
-  const int side = mode == OASES_OVERLAP_FINE ? 1 : 0;
+  const int side = (mode == OASES_OVERLAP_FINE || mode == OASES_OVERLAP_FUSED) ? 1 : 0;
   for (int l = 0; l < L; ++l)
     for (int sb = 0; sb < 2; ++sb) {
       ops.push_back({OP_F, l, sb, 0});
@@ -183,7 +183,7 @@ struct oases_ctx {
   hipStream_t cs = nullptr, ss = nullptr;
   bool streams_set = false;
   std::vector<hipEvent_t> evF, evCF, evBdX, evCB;
-  hipGraphExec_t gexec[4] = {nullptr, nullptr, nullptr, nullptr};
+  hipGraphExec_t gexec[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
   std::vector<uint8_t> fwd_done, bwd_done;
   std::string err;
   // timing instrumentation
@@ -219,6 +219,10 @@ struct Exec {
   const WsLayout &W;
   int mode;
   bool overlap;  // side stream distinct from the compute stream
+  // OVERLAP_FUSED (bf16): an AllReduce point waits here and runs as extra
+  // workgroups of the next GEMM launched on the compute stream
+  bool fused = false;
+  FusedSum pending{};
 
   char *ws() const { return static_cast<char *>(c->buf.workspace); }
   const Dims &D() const { return c->D; }
@@ -272,9 +276,25 @@ struct Exec {
 
   int gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmArgs &g, hipStream_t s);
   int sum(const void *own, const void *pr, void *out, hipStream_t s) {
+    if (fused) {  // deferred to the next GEMM launch (flush_pending at the latest)
+      const int64_t n = (int64_t)D().T * D().h;
+      pending = FusedSum{own, pr, n, out, n / 8, D().w - 1, allreduce_fused_wgs(n / 8)};
+      return OASES_OK;
+    }
     if (int r = prof_begin(KC_SUM, s)) return r;
     HIPX(allreduce_point(bf16(), own, pr, (int64_t)D().T * D().h, D().w - 1, out, (int64_t)D().T * D().h, s));
     return prof_end(KC_SUM, s);
+  }
+
+  // a deferred sum with no GEMM after it runs as its own kernel
+  int flush_pending() {
+    if (!pending.wgs) return OASES_OK;
+    const FusedSum f = pending;
+    pending = FusedSum{};
+    fused = false;
+    const int r = sum(f.own, f.peers, f.out, c->cs);
+    fused = true;
+    return r;
   }
 
   // column part of block l (F or R): writes the slot's activations.
@@ -420,7 +440,12 @@ struct Exec {
   }
 };
 
-int Exec::gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmArgs &g, hipStream_t s) {
+int Exec::gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmArgs &g0, hipStream_t s) {
+  GemmArgs g = g0;
+  if (fused && pending.wgs && s == c->cs && g.M > 0 && g.N > 0) {
+    g.sum = pending;
+    pending = FusedSum{};
+  }
   if (int r = prof_begin(cls, s)) return r;
   if (bf16()) HIPX(gemm_bf16(la, lb, epi, g, s));
   else HIPX(gemm_f32(la, lb, epi, g, s));
@@ -451,8 +476,10 @@ int need_ready(oases_ctx *c, int mode) {
 int issue_ops(oases_ctx *c, int mode, const std::vector<Op> &ops) {
   const WsLayout W = make_layout(c->D, mode);
   Exec ex{c, W, mode, mode == OASES_OVERLAP_FINE && c->ss != c->cs};
+  ex.fused = mode == OASES_OVERLAP_FUSED && c->D.dtype == OASES_BF16;
   for (const Op &o : ops)
     if (int r = ex.run(o)) return r;
+  if (int r = ex.flush_pending()) return r;
   if (ex.overlap) {  // join the side stream into the compute stream
     HIPX(hipStreamWaitEvent(c->cs, c->evCB[0 * 2 + 1], 0));
   }
@@ -487,7 +514,7 @@ int oases_create(const oases_config *cfg, oases_ctx **out) {
 
 int oases_workspace_bytes(const oases_config *cfg, int32_t mode, size_t *bytes) {
   if (!bytes) return OASES_E_ARG;
-  if (mode < 0 || mode > 3) return OASES_E_ARG;
+  if (mode < 0 || mode > 4) return OASES_E_ARG;
   Dims d;
   if (int r = check_config(cfg, &d, nullptr)) return r;
   *bytes = make_layout(d, mode).total;
@@ -590,7 +617,7 @@ int layer_bwd_recompute(oases_ctx *c, int32_t layer, int32_t sub_batch) {
 
 int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph) {
   if (!c) return OASES_E_ARG;
-  if (mode < 0 || mode > 3) return set_err(c, OASES_E_ARG, "bad mode");
+  if (mode < 0 || mode > 4) return set_err(c, OASES_E_ARG, "bad mode");
   if (int r = need_ready(c, mode)) return r;
   const std::vector<Op> ops = build_ops(c->D.L, mode);
   std::fill(c->fwd_done.begin(), c->fwd_done.end(), 0);
@@ -619,7 +646,7 @@ int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph) {
 
 int oases_schedule_ops(const oases_ctx *c, int32_t mode, int32_t *ops, int32_t cap, int32_t *n_ops) {
   if (!c || !n_ops || (cap > 0 && !ops) || cap < 0) return OASES_E_ARG;
-  if (mode < 0 || mode > 3) return OASES_E_ARG;
+  if (mode < 0 || mode > 4) return OASES_E_ARG;
   const std::vector<Op> v = build_ops(c->D.L, mode);
   *n_ops = (int32_t)v.size();
   for (int i = 0; i < (int)v.size() && i < cap; ++i) {

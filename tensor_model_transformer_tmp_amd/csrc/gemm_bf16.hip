@@ -211,6 +211,79 @@ __device__ __forceinline__ void epilogue_row(const GemmArgs &g, int m, const int
     }
 }
 
+// ---- AllReduce-point sum on extra workgroups of a GEMM launch --------------
+//
+// Workgroup w of g.sum.wgs streams vectors w*T + t, w*T + t + stride, ...
+// (T threads, 8 bf16 per vector): all peers of UNROLL vectors are loaded four
+// at a time before their adds, in the order own, peer 0, peer 1, ... with one
+// rounding -- the arithmetic of the standalone sum kernel, so results are
+// bit-identical to it.
+__device__ __forceinline__ uint4 nt_load(const uint4 *p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void add8(float (&a)[8], const uint4 &b) {
+  a[0] += lo_f32(b.x); a[1] += hi_f32(b.x); a[2] += lo_f32(b.y); a[3] += hi_f32(b.y);
+  a[4] += lo_f32(b.z); a[5] += hi_f32(b.z); a[6] += lo_f32(b.w); a[7] += hi_f32(b.w);
+}
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ void fused_sum(const FusedSum &f, int wg) {
+  constexpr int UNROLL = 2;
+  const int64_t stride = (int64_t)f.wgs * blockDim.x;
+  const uint4 *own = static_cast<const uint4 *>(f.own);
+  const uint4 *peers = static_cast<const uint4 *>(f.peers);
+  const int64_t pstride = f.peer_stride / 8;
+  for (int64_t v0 = (int64_t)wg * blockDim.x + threadIdx.x; v0 < f.nvec; v0 += stride * UNROLL) {
+    float acc[UNROLL][8];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t v = v0 + u * stride;
+      const uint4 a = v < f.nvec ? nt_load(own + v) : make_uint4(0, 0, 0, 0);
+      acc[u][0] = lo_f32(a.x); acc[u][1] = hi_f32(a.x); acc[u][2] = lo_f32(a.y); acc[u][3] = hi_f32(a.y);
+      acc[u][4] = lo_f32(a.z); acc[u][5] = hi_f32(a.z); acc[u][6] = lo_f32(a.w); acc[u][7] = hi_f32(a.w);
+    }
+    int k = 0;
+    for (; k + 4 <= f.np; k += 4) {
+      uint4 b[4][UNROLL];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int64_t v = v0 + u * stride;
+          b[q][u] = v < f.nvec ? nt_load(peers + (k + q) * pstride + v) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) add8(acc[u], b[q][u]);
+    }
+    for (; k < f.np; ++k) {
+      uint4 b[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int64_t v = v0 + u * stride;
+        b[u] = v < f.nvec ? nt_load(peers + k * pstride + v) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) add8(acc[u], b[u]);
+    }
+    uint4 *out = static_cast<uint4 *>(f.out);
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t v = v0 + u * stride;
+      if (v < f.nvec)
+        out[v] = make_uint4(cvt_pk_bf16(acc[u][0], acc[u][1]), cvt_pk_bf16(acc[u][2], acc[u][3]),
+                            cvt_pk_bf16(acc[u][4], acc[u][5]), cvt_pk_bf16(acc[u][6], acc[u][7]));
+    }
+  }
+}
+
 // ---- kernel -----------------------------------------------------------------
 
 template <int B, int E, class F>
@@ -250,6 +323,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) bf16_t sA[STAGES][BM * BK];
   __shared__ __attribute__((aligned(1024))) bf16_t sB[STAGES][BN * BK];
 
+  // the first g.sum.wgs workgroups run a fused AllReduce-point sum
+  if ((int)blockIdx.x < g.sum.wgs) {
+    fused_sum(g.sum, blockIdx.x);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;  // hl: which 32-lane half
@@ -259,7 +337,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   // tiles, grouped 8 m-tiles at a time along n, so an XCD's L2 sees reuse
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
-  int bid = blockIdx.x;
+  int bid = blockIdx.x - g.sum.wgs;  // sum.wgs is a multiple of 8: XCD round robin unchanged
   if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
   constexpr int GROUP = 8;
   const int group_span = GROUP * tiles_n;
@@ -375,7 +453,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
 template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI, int BK = 64>
 hipError_t launch(const GemmArgs &g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  OASES_LAUNCH((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, BK, LA, LB, EPI>), dim3(tiles),
+  OASES_LAUNCH((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, BK, LA, LB, EPI>), dim3(tiles + g.sum.wgs),
                      dim3(64 * WGM * WGN), s, g);
   return hipGetLastError();
 }

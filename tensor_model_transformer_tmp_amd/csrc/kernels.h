@@ -54,6 +54,19 @@ enum Epi : int {
 // (k contiguous), MC = stored [K][ldb] (n contiguous).
 enum Layout : int { KC = 0, MC = 1 };
 
+// An AllReduce-point sum (out = own + peers[0..np), float32 adds in that
+// order, one rounding) that a GEMM launch runs on extra workgroups beside its
+// tiles (sum_wgs of them; none when 0).  Same arithmetic as allreduce_point.
+struct FusedSum {
+  const void *own;
+  const void *peers;
+  int64_t peer_stride;  // elements between peers
+  void *out;
+  int64_t nvec;         // 8-element vectors (n / 8)
+  int np;
+  int wgs;
+};
+
 struct GemmArgs {
   int M, N, K;
   const void *A;
@@ -68,6 +81,7 @@ struct GemmArgs {
   const void *aux;
   int ld_aux;
   int beta;
+  FusedSum sum;  // bf16 GEMMs only
 };
 
 // C[M,N] = sum_k A(m,k) B(k,n) with the given layouts and epilogue.
@@ -81,6 +95,9 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
                            int n_peers, void *out, int64_t n, hipStream_t s);
 // largest grid (workgroups) of the AllReduce-point kernel
 void allreduce_set_grid_cap(int cap);
+// workgroups that run an AllReduce point of nvec 8-element vectors fused into
+// a GEMM launch (a multiple of 8, at most half the grid cap)
+int allreduce_fused_wgs(int64_t nvec);
 
 // db (+)= column sums of x[rows, cols] in a fixed order; partial needs
 // colsum_partial_floats(rows, cols) floats.

@@ -137,4 +137,6 @@ def test_op_lists_match_oracle_schedules(n_layers):
     ctx = shard.ShardContext(cfg)
     for mode in oschedule.MODES:
         assert ctx.schedule_ops(mode) == oschedule.build_ops(n_layers, mode), mode
+    # the fused overlap runs the overlapped op list (sums on the next GEMM launch)
+    assert ctx.schedule_ops("overlap_fused") == oschedule.build_ops(n_layers, "overlap_fine")
     ctx.close()

@@ -1,6 +1,7 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (overlapped fine-grained schedule, eager on two streams, automatic tile
-and kernel-layout choice), against the complete float64 oracle step on the
+times (overlapped fine-grained schedule, eager on two streams, and the fused
+overlap in which the sums run on the next GEMM launch; automatic tile and
+kernel-layout choice), against the complete float64 oracle step on the
 same seeded inputs: every element of Y, dX and every weight / bias gradient.
 
 Each workload runs with zero peer partials, so the shard's own outputs
@@ -51,10 +52,11 @@ def test_full_size_step_matches_oracle(name, zero_peers):
     cfg = gen.PRESETS[name]
     inp = gen.make_inputs(cfg, zero_peers=zero_peers)
     print(f"\n[{name} zero_peers={zero_peers}] device step", flush=True)
-    dev = DeviceShard(inp, modes=("overlap_fine", "serial_fine"))
+    dev = DeviceShard(inp, modes=("overlap_fine", "overlap_fused", "serial_fine"))
     dev.step("overlap_fine", use_graph=False)
     got = dev.results()
-    for mode, graph in (("overlap_fine", True), ("overlap_fine", True), ("serial_fine", False)):
+    for mode, graph in (("overlap_fine", True), ("overlap_fine", True), ("overlap_fused", False),
+                        ("overlap_fused", True), ("overlap_fused", True), ("serial_fine", False)):
         dev.step(mode, use_graph=graph)
         _bitwise_equal(dev.results(), got, f"{name} {mode} graph={graph}")
     dev.close()
