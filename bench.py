@@ -66,7 +66,8 @@ def step_flops(cfg):
 # Algorithmic work of one launch of each kernel class (averaged over the
 # class's launches in a step).  A class is what the executor brackets with one
 # pair of HIP events: one GEMM, one attention forward, one attention backward
-# (delta + dK/dV + dQ kernels), one AllReduce-point sum, one bias column sum.
+# (delta + dK/dV + dQ kernels), one AllReduce-point sum, one bias column sum
+# (float32 only: in bf16 the dW_in GEMM sums its A operand's columns).
 KERNEL_CLASSES = ("gemm_fwd", "gemm_dx", "gemm_dw", "attn_fwd", "attn_bwd", "sum", "colsum")
 
 
@@ -97,8 +98,8 @@ def class_work(cfg, kclass):
             tot += 2 * 4 * att
         elif kclass == "sum":
             tot += 2 * 2 * (cfg.tmp_width + 1) * T * h * esz
-        elif kclass == "colsum":     # read dpre once, read-modify-write db
-            tot += 2 * (T * nin * esz + 2 * nin * 4)
+        elif kclass == "colsum" and cfg.dtype != gen.BF16:  # bf16: inside the dW_in GEMM
+            tot += 2 * (T * nin * esz + 2 * nin * 4)         # read dpre once, db read-modify-write
     return tot, ("B" if kclass in ("sum", "colsum") else "FLOP")
 
 

@@ -220,9 +220,12 @@ int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int
  *   b_layout 0: B stored [N][ldb] (k contiguous);  1: B stored [K][ldb] (n contiguous)
  *   epilogue 0: C = acc;  1: C = acc + bias[n];  2: C = gelu(acc + bias[n]) and, if pre
  *            != NULL, pre = acc + bias[n];  3: C = acc * gelu'(aux[m][n]);
- *            4: C (float32) = acc, plus the old C when beta != 0.
+ *            4: C (float32) = acc, plus the old C when beta != 0;
+ *            5 (bfloat16 only): as 4, and pre (float32, m elements) = the sums of
+ *            A(m, k) over k, plus the old pre when beta != 0 (a bias gradient
+ *            taken beside its weight gradient).
  * Supported: layouts (0,0) with epilogues 0-2 (forward / recompute), (0,1) with
- * 0 and 3 (data gradient), (1,1) with 4 (weight gradient).  Storage-type
+ * 0 and 3 (data gradient), (1,1) with 4 and 5 (weight gradient).  Storage-type
  * operands; the contiguous dimension of every operand and N are multiples of
  * 8; leading dimensions in elements, multiples of 8.  pre and C (epilogues
  * 0-3) use ldc; aux uses ld_aux. */

@@ -419,6 +419,10 @@ struct Exec {
     g2.M = nin; g2.N = d.h; g2.K = d.T;
     g2.A = dpre; g2.lda = nin; g2.B = layer_in(l, sb); g2.ldb = d.h;
     g2.C = p.dw_in; g2.ldc = d.h; g2.beta = sb;
+    if (bf16()) {  // db_in (+)= column sums of dpre, computed by the same GEMM
+      g2.colsum = static_cast<float *>(p.db_in);
+      return gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, c->cs);
+    }
     if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, c->cs)) return r;
     if (int r = prof_begin(KC_COLSUM, c->cs)) return r;
     HIPX(colsum(bf16(), dpre, d.T, nin, nin, reinterpret_cast<float *>(ws() + W.colsum),
@@ -730,13 +734,14 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
   const bool fwd = a_layout == 0 && b_layout == 0, dx = a_layout == 0 && b_layout == 1,
              dw = a_layout == 1 && b_layout == 1;
   if (!((fwd && epilogue >= 0 && epilogue <= 2) || (dx && (epilogue == 0 || epilogue == 3)) ||
-        (dw && epilogue == 4)))
+        (dw && (epilogue == 4 || (epilogue == 5 && dtype == OASES_BF16)))))
     return OASES_E_UNSUPPORTED;
   if (m < 0 || n < 0 || k < 0 || n % 8) return OASES_E_ARG;
   if (m == 0 || n == 0) return OASES_OK;
   if (!a || !b || !c_) return OASES_E_ARG;
   if ((epilogue == 1 || epilogue == 2) && !bias) return OASES_E_ARG;
   if (epilogue == 3 && (!aux || ld_aux < n || ld_aux % 8)) return OASES_E_ARG;
+  if (epilogue == 5 && (!pre || ((uintptr_t)pre & 3))) return OASES_E_ARG;
   // contiguous dimension of each operand: A: k (layout 0) or m (1); B: k (0) or n (1)
   const int a_cont = a_layout == 0 ? k : m, a_rows = a_layout == 0 ? m : k;
   const int b_cont = b_layout == 0 ? k : n, b_rows = b_layout == 0 ? n : k;
@@ -744,14 +749,15 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
   if (a_cont % 8 || b_cont % 8 || lda < a_cont || ldb < b_cont || ldc < n || lda % 8 || ldb % 8 ||
       ldc % 8)
     return OASES_E_ARG;
-  if (!aligned16(a) || !aligned16(b) || !aligned16(c_) || (pre && !aligned16(pre)) ||
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c_) || (pre && epilogue != 5 && !aligned16(pre)) ||
       (aux && !aligned16(aux)) || (bias && ((uintptr_t)bias & 7)))
     return OASES_E_ALIGN;
   GemmArgs g{};
   g.M = m; g.N = n; g.K = k; g.A = a; g.lda = lda; g.B = b; g.ldb = ldb; g.C = c_; g.ldc = ldc;
   g.bias = bias; g.pre = pre; g.ld_pre = ldc; g.aux = aux; g.ld_aux = ld_aux; g.beta = beta;
   const oases::Layout la = a_layout ? MC : KC, lb = b_layout ? MC : KC;
-  const Epi epi = static_cast<Epi>(epilogue);
+  if (epilogue == 5) { g.colsum = static_cast<float *>(pre); g.pre = nullptr; }
+  const Epi epi = static_cast<Epi>(epilogue == 5 ? 4 : epilogue);
   const hipError_t e = dtype == OASES_BF16 ? gemm_bf16(la, lb, epi, g, static_cast<hipStream_t>(stream))
                                            : gemm_f32(la, lb, epi, g, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? OASES_OK : OASES_E_HIP;

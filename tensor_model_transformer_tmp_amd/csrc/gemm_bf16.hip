@@ -28,6 +28,10 @@
 namespace oases {
 namespace {
 
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// EPI_F32 that also stores the column sums of A in GemmArgs::colsum
+constexpr int EPI_F32_COLSUM = 16;
+
 // A k tile is BK = 64 or 32 elements deep (a kernel template parameter): 64
 // for the 2-3 stage pipelines, 32 to fit 4-5 stages of the largest tiles in
 // the 160 KB of LDS.
@@ -362,6 +366,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
     tb.issue(B, g.ldb, n0, stage * BK, g.K, lds_addr(slotB(I)), wave, lane);
   };
   f32x16 acc[TN][TM];
+  // column sums of A over k (bias gradient beside a weight gradient): every
+  // wave adds up the A fragments it feeds the MFMAs, lane half hl holding
+  // k = 8 hl .. 8 hl + 7 of each 16-k substep, and the waves of the first n
+  // tile store them.  A compile-time variant: a runtime branch between the
+  // MFMAs and the accumulator reads of the epilogue is not allowed here.
+  constexpr bool COL = EPI == EPI_F32_COLSUM;
+  float csum[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) csum[i] = 0.f;
 #pragma unroll
   for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -401,6 +414,19 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int i2 = 0; i2 < TM; ++i2) acc[j][i2] = mfma32(wb[ks & 1][j], xa[ks & 1][i2], acc[j][i2]);
+      if constexpr (COL) {
+        const bf16x2v one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int i2 = 0; i2 < TM; ++i2) {
+          const uint4 u = __builtin_bit_cast(uint4, xa[ks & 1][i2]);
+          float c = csum[i2];
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.x), one, c, false);
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.y), one, c, false);
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.z), one, c, false);
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.w), one, c, false);
+          csum[i2] = c;
+        }
+      }
     }
     // schedule: fragment reads of substep 0, then each MFMA of substep ks
     // followed by one LDS read of substep ks+1
@@ -446,7 +472,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) v[j][jj][ii] = acc[j][i][jj * 4 + ii];
-    epilogue_row<EPI, TN>(g, m, ncol, v);
+    epilogue_row<COL ? (int)EPI_F32 : EPI, TN>(g, m, ncol, v);
+  }
+  if constexpr (COL) {
+    if (tn == 0 && wn == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const float total = csum[i] + __shfl_xor(csum[i], 32);  // k halves 0..7 + 8..15
+        const int m = m0 + wm * WTM + i * 32 + l32;
+        if (hl == 0 && m < g.M) g.colsum[m] = (g.beta ? g.colsum[m] : 0.f) + total;
+      }
+    }
   }
 }
 
@@ -529,7 +565,8 @@ hipError_t gemm_bf16(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream
       default: break;
     }
   } else if (la == MC && lb == MC) {
-    if (epi == EPI_F32) return dispatch_tile<MC, MC, EPI_F32>(g, s);
+    if (epi == EPI_F32)
+      return g.colsum ? dispatch_tile<MC, MC, EPI_F32_COLSUM>(g, s) : dispatch_tile<MC, MC, EPI_F32>(g, s);
   }
   return hipErrorInvalidValue;
 }

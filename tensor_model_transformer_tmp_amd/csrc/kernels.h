@@ -82,6 +82,10 @@ struct GemmArgs {
   int ld_aux;
   int beta;
   FusedSum sum;  // bf16 GEMMs only
+  // bf16 GEMMs with A stored [K][lda] (m contiguous) only: colsum[m] =
+  // (beta ? colsum[m] : 0) + sum over k of A(m, k), float32 -- the bias
+  // gradient of a weight-gradient GEMM (none when null)
+  float *colsum;
 };
 
 // C[M,N] = sum_k A(m,k) B(k,n) with the given layouts and epilogue.

@@ -238,7 +238,7 @@ def allreduce_point(dtype, own, peers, n_peers, out, stream=None):
                 "oases_allreduce_point")
 
 
-EPILOGUES = {"store": 0, "bias": 1, "gelu": 2, "gelu_bwd": 3, "f32": 4}
+EPILOGUES = {"store": 0, "bias": 1, "gelu": 2, "gelu_bwd": 3, "f32": 4, "f32_colsum": 5}
 
 
 def gemm(dtype, a, b, c, a_layout=0, b_layout=0, epilogue="store", m=None, n=None, k=None,

@@ -122,6 +122,11 @@ def test_single_kernel_entry_validation():
     # bias epilogue without a bias
     assert L.oases_gemm(1, 0, 0, 1, 4, 16, 16, 16, 16, 32, 16, 48, 16, None, None, None, 0, 0,
                         None) == shard.E_ARG
+    # column-sum epilogue: bfloat16 only, needs its float32 output in pre
+    assert L.oases_gemm(0, 1, 1, 5, 4, 16, 16, 16, 16, 32, 16, 48, 16, None, 64, None, 0, 0,
+                        None) == shard.E_UNSUPPORTED
+    assert L.oases_gemm(1, 1, 1, 5, 4, 16, 16, 16, 16, 32, 16, 48, 16, None, None, None, 0, 0,
+                        None) == shard.E_ARG
     # empty problem is a no-op
     assert L.oases_gemm(1, 0, 0, 0, 0, 16, 16, 16, 16, 32, 16, 48, 16, None, None, None, 0, 0,
                         None) == shard.OK

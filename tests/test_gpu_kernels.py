@@ -114,7 +114,7 @@ GEMM_SHAPES = [(200, 192, 128), (1000, 520, 576), (2048, 1024, 1024), (296, 136,
 
 
 @pytest.mark.parametrize("variant", list(range(20)))
-@pytest.mark.parametrize("kind", ["fwd", "dx", "dx_gelu", "dw"])
+@pytest.mark.parametrize("kind", ["fwd", "dx", "dx_gelu", "dw", "dw_colsum"])
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 def test_gemm_layouts_and_tiles(variant, kind, m, n, k):
     """Every operand layout / epilogue of the step's GEMMs and every tile
@@ -147,12 +147,19 @@ def test_gemm_layouts_and_tiles(variant, kind, m, n, k):
             b_kn = np.ascontiguousarray(b_nk.T)
             old = rng.standard_normal((m, n)).astype(np.float32)
             c = torch.from_numpy(old).to(dev)
+            cs = None
+            if kind == "dw_colsum":   # plus the sums of A over k, added to old values
+                old_cs = rng.standard_normal(m).astype(np.float32)
+                cs = torch.from_numpy(old_cs).to(dev)
             shard.gemm(shard.BF16, to_device(a_mk, gen.BF16, dev), to_device(b_kn, gen.BF16, dev), c,
-                       1, 1, "f32", m=m, n=n, k=k, beta=1)
+                       1, 1, "f32_colsum" if cs is not None else "f32", m=m, n=n, k=k, pre=cs, beta=1)
             ref = ref + old
         torch.cuda.synchronize()
         got = c.cpu().numpy() if c.dtype == torch.float32 else gen.bf16_bits_to_f64(to_storage(c))
-        tol = 1e-5 if kind == "dw" else 8e-3
+        tol = 1e-5 if kind.startswith("dw") else 8e-3
         assert_close(got, ref, tol, f"{kind} {m}x{n}x{k} variant {variant}")
+        if kind == "dw_colsum":
+            assert_close(cs.cpu().numpy(), af.sum(axis=1) + old_cs, 1e-5,
+                         f"column sums {m}x{n}x{k} variant {variant}")
     finally:
         shard.set_gemm_tile_variant(0)
