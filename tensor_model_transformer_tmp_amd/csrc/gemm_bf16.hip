@@ -407,9 +407,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
       for (int j = 0; j < TN; ++j) wb[buf][j] = TB::frag(b_s, wn * WTN + j * 32 + l32, ks, hl);
     };
     read_frags(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) read_frags(ks + 1, (ks + 1) & 1);
+    // k substeps unrolled at compile time, so every fragment and accumulator
+    // index is a constant before the register promotion of local arrays
+    static_for<0, BK / 16>([&](auto KS) {
+      constexpr int ks = decltype(KS)::value;
+      if constexpr (ks + 1 < BK / 16) read_frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -427,7 +429,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
           csum[i2] = c;
         }
       }
-    }
+    });
     // schedule: fragment reads of substep 0, then each MFMA of substep ks
     // followed by one LDS read of substep ks+1
     constexpr int RD = TM * (LA == KC ? 1 : 2) + TN * (LB == KC ? 1 : 2), MF = TM * TN;
