@@ -159,6 +159,126 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": 2 * n, "launches": 3}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# studies (one JSON line each; not the timed step)
+# ---------------------------------------------------------------------------
+
+ABLATION_MODES = ("serial_norecompute", "serial_default", "serial_fine", "overlap_fine",
+                  "overlap_fused")
+
+
+def study_ablation(cfg, steps, warmup):
+    """Schedule ablation on one GPU with the same kernels (Section IV, Fig. 4;
+    the analogue of the pages' schedule comparison table): no recompute
+    (every intermediate kept), default recompute (the whole block re-run,
+    row GEMM and its AllReduce point included), fine-grained recompute
+    serial, and fine-grained recompute overlapped (side stream, or fused into
+    the next GEMM launch).  Each mode is timed eagerly and as a hipGraph
+    replay; the faster is reported.  ``model_tflops`` divides the model's own
+    forward + backward FLOPs (no recompute) by the step time, so the modes are
+    compared on equal work; ``executed_tflops`` counts what the mode runs."""
+    import torch
+    from tensor_model_transformer_tmp_amd.device import DeviceShard
+
+    dev = DeviceShard(gen.make_inputs(cfg), device="cuda:0", modes=ABLATION_MODES)
+    f, r, b = step_flops(cfg)
+    executed = {"serial_norecompute": f + b, "serial_default": 2 * f + b}
+    out = {}
+    for mode in ABLATION_MODES:
+        best = None
+        for graph in (False, True):
+            for _ in range(warmup):
+                dev.ctx.schedule_step(mode, graph)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                dev.ctx.schedule_step(mode, graph)
+            torch.cuda.synchronize()
+            t = (time.perf_counter() - t0) / steps
+            if best is None or t < best[0]:
+                best = (t, graph)
+        t, graph = best
+        ex = executed.get(mode, f + r + b)
+        out[mode] = {"ms_per_step": t * 1e3, "issue": "hipGraph" if graph else "eager",
+                     "model_tflops": (f + b) / t / 1e12, "executed_gflop": ex / 1e9,
+                     "executed_tflops": ex / t / 1e12}
+    dev.close()
+    base = out["serial_norecompute"]["ms_per_step"]
+    for v in out.values():
+        v["speed_vs_norecompute"] = base / v["ms_per_step"]
+    return {"study": "schedule_ablation", "workload": cfg.name, "steps": steps,
+            "warmup": warmup, "modes": out}
+
+
+def _layer_gemms(cfg, l, T):
+    """The six GEMMs of block l over T tokens: (name, a_layout, b_layout, M, N, K)."""
+    h, nin, nmid = cfg.hidden, cfg.n_in(l), cfg.n_mid(l)
+    return [("col_fwd", 0, 0, T, nin, h), ("row_fwd", 0, 0, T, h, nmid),
+            ("row_dx", 0, 1, T, nmid, h), ("col_dx", 0, 1, T, h, nin),
+            ("row_dw", 1, 1, h, nmid, T), ("col_dw", 1, 1, nin, h, T)]
+
+
+def study_density(names, reps=20):
+    """Batch-split density study (Section IV's argument that splitting a
+    micro-batch in two costs little arithmetic density): every GEMM of each
+    block at the whole micro-batch (T = B*s tokens) and at one sub-batch
+    (T/2), on the same kernels with the automatic tile choice.  Each is timed
+    as a hipGraph of ``reps`` back-to-back launches (no host launch cost);
+    ``split_loss`` = 1 - t(T) / (2 t(T/2)) summed over the block's GEMMs."""
+    import torch
+    from tensor_model_transformer_tmp_amd import shard
+
+    dev = torch.device("cuda:0")
+    res = []
+    for name in names:
+        cfg = gen.PRESETS[name]
+        kinds = sorted(set(cfg.blocks), key=cfg.blocks.index)
+        for kind in kinds:
+            l = cfg.blocks.index(kind)
+            row = {"workload": name, "block": "attn" if kind == gen.ATTN else "ffn", "gemms": {}}
+            tot = {}
+            for T in (2 * cfg.t_sb, cfg.t_sb):
+                tot[T] = 0.0
+                for gname, la, lb, M, N, K in _layer_gemms(cfg, l, T):
+                    a = torch.randn(K * M, device=dev).to(torch.bfloat16).view(
+                        (M, K) if la == 0 else (K, M))
+                    b = torch.randn(K * N, device=dev).to(torch.bfloat16).view(
+                        (N, K) if lb == 0 else (K, N))
+                    c = torch.empty(M, N, device=dev,
+                                    dtype=torch.float32 if la == 1 else torch.bfloat16)
+                    epi = "f32" if la == 1 else "store"
+                    s = torch.cuda.Stream(device=dev)
+
+                    def launch():
+                        shard.gemm(shard.BF16, a, b, c, la, lb, epi, m=M, n=N, k=K, stream=s)
+
+                    with torch.cuda.stream(s):
+                        launch()
+                    torch.cuda.synchronize()
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=s):
+                        for _ in range(reps):
+                            launch()
+                    g.replay()
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    with torch.cuda.stream(s):
+                        e0.record(s)
+                        g.replay()
+                        e1.record(s)
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) / reps * 1e3
+                    del g
+                    tot[T] += us
+                    row["gemms"].setdefault(gname, {})[f"T{T}"] = {
+                        "shape": [M, N, K], "us": us, "tflops": gemm_flops(M, N, K) / us / 1e6}
+            T = 2 * cfg.t_sb
+            row["us_whole"], row["us_two_halves"] = tot[T], 2 * tot[cfg.t_sb]
+            row["split_loss"] = 1.0 - tot[T] / (2 * tot[cfg.t_sb])
+            res.append(row)
+    return {"study": "batch_split_density", "reps": reps, "blocks": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +290,9 @@ def main():
                     help="kernel class for the roofline entry (default: most time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES three times (counter calibration)")
+    ap.add_argument("--study", choices=("ablation", "density"), default=None,
+                    help="run a study instead of the timed step: schedule ablation on --config, "
+                         "or the batch-split GEMM density study over the bf16 workloads")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
@@ -178,6 +301,14 @@ def main():
               "(the AllReduce points are emulated with resident peer buffers on one GPU)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.study == "ablation":
+        print(json.dumps(study_ablation(gen.PRESETS[args.config], args.steps, args.warmup)), flush=True)
+        return 0
+    if args.study == "density":
+        names = [n for n in gen.PRESET_ORDER if gen.PRESETS[n].dtype == gen.BF16]
+        print(json.dumps(study_density(names)), flush=True)
+        return 0
 
     import torch
     from tensor_model_transformer_tmp_amd.device import DeviceShard
