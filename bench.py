@@ -66,7 +66,7 @@ def step_flops(cfg):
 # Algorithmic work of one launch of each kernel class (averaged over the
 # class's launches in a step).  A class is what the executor brackets with one
 # pair of HIP events: one GEMM, one attention forward, one attention backward
-# (delta + dK/dV + dQ kernels), one AllReduce-point sum, one bias column sum
+# (dQ-with-delta + dK/dV kernels), one AllReduce-point sum, one bias column sum
 # (float32 only: in bf16 the dW_in GEMM sums its A operand's columns).
 KERNEL_CLASSES = ("gemm_fwd", "gemm_dx", "gemm_dw", "attn_fwd", "attn_bwd", "sum", "colsum")
 

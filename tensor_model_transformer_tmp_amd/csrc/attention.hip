@@ -34,10 +34,11 @@
 // units), so an unscaled probability is at most 2^8.  l and O share that
 // reference, so the result is the same softmax; only the rounding differs.
 //
-// Backward (no atomics): delta = rowsum(dO * O); the dK/dV kernel owns keys
-// and walks query blocks (S = Q K^T, dP = dO V^T, dV^T += dO^T P,
-// dK^T += Q^T dS); the dQ kernel owns queries and walks key blocks
-// (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T).  P is rebuilt from lse.
+// Backward (no atomics): the dQ kernel owns queries, computes their
+// delta = rowsum(dO * O) (stored for the next kernel) and walks key blocks
+// (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T); the dK/dV kernel then owns
+// keys and walks query blocks (S = Q K^T, dP = dO V^T, dV^T += dO^T P,
+// dK^T += Q^T dS).  P is rebuilt from lse.
 #include <math.h>
 
 #include "common.h"
@@ -390,32 +391,6 @@ __global__ void __launch_bounds__(64 * NW)
 }
 
 // ---------------------------------------------------------------------------
-// backward: delta = rowsum(dO * O) per (sequence, head, query)
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256)
-    attn_delta_kernel(const bf16_t *__restrict__ o, const bf16_t *__restrict__ dout,
-                      float *__restrict__ delta, int nb, int s, int s_pad, int nh) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, t, h), h fastest
-  if (idx >= (int64_t)nb * s * nh) return;
-  const int h = idx % nh;
-  const int64_t row = idx / nh;  // b*s + t
-  const int a = nh * D;
-  const bf16_t *po = o + row * a + h * D, *pd = dout + row * a + h * D;
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const uint4 x = *reinterpret_cast<const uint4 *>(po + c);
-    const uint4 y = *reinterpret_cast<const uint4 *>(pd + c);
-    acc += lo_f32(x.x) * lo_f32(y.x) + hi_f32(x.x) * hi_f32(y.x) + lo_f32(x.y) * lo_f32(y.y) +
-           hi_f32(x.y) * hi_f32(y.y) + lo_f32(x.z) * lo_f32(y.z) + hi_f32(x.z) * hi_f32(y.z) +
-           lo_f32(x.w) * lo_f32(y.w) + hi_f32(x.w) * hi_f32(y.w);
-  }
-  const int b = (int)(row / s), t = (int)(row % s);
-  delta[((int64_t)b * nh + h) * s_pad + t] = acc;
-}
-
-// ---------------------------------------------------------------------------
 // backward: dK, dV.  A wave owns 32 keys and walks 32-query blocks of Q and dO
 // (plus their lse and delta) from the first block its keys are visible to.
 // ---------------------------------------------------------------------------
@@ -599,8 +574,8 @@ __global__ void __launch_bounds__(64 * NW)
 // ---------------------------------------------------------------------------
 template <int D, int OWN>
 __global__ void __launch_bounds__(64 * NW)
-    attn_dq_kernel(const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout,
-                   const float *__restrict__ lse, const float *__restrict__ delta,
+    attn_dq_kernel(const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ o, const bf16_t *__restrict__ dout,
+                   const float *__restrict__ lse, float *__restrict__ delta,
                    bf16_t *__restrict__ dqkv, int s, int s_pad, int nh, int causal, float scale_log2,
                    float scale) {
   using B = Blk<D>;
@@ -624,14 +599,30 @@ __global__ void __launch_bounds__(64 * NW)
 
   bf16x8 qf[D / 16], df[D / 16];
   const int qrow = min(qi, s - 1);
+  const bf16_t *Op = o + (int64_t)b * s * a + h * D + (int64_t)qrow * a + hl * 8;
+  uint4 of[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     qf[kk] = load_frag(Qp + (int64_t)qrow * ld + kk * 16 + hl * 8);
     df[kk] = load_frag(dOp + (int64_t)qrow * a + kk * 16 + hl * 8);
+    of[kk] = *reinterpret_cast<const uint4 *>(Op + kk * 16);
   }
   const bool q_ok = qi < s;
   const float lse2 = q_ok ? lse[(int64_t)bh * s_pad + qi] * LOG2E : 0.f;
-  const float dlt = q_ok ? delta[(int64_t)bh * s_pad + qi] : 0.f;
+  // delta = rowsum(dO * O) of this lane's query: the lane holds half of the
+  // row's d values (the same half of dO as its dQ fragments), the lane 32
+  // away the other half.  Stored once per query for the dK/dV kernel.
+  float part = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint4 x = of[kk], y = __builtin_bit_cast(uint4, df[kk]);
+    part += lo_f32(x.x) * lo_f32(y.x) + hi_f32(x.x) * hi_f32(y.x) + lo_f32(x.y) * lo_f32(y.y) +
+            hi_f32(x.y) * hi_f32(y.y) + lo_f32(x.z) * lo_f32(y.z) + hi_f32(x.z) * hi_f32(y.z) +
+            lo_f32(x.w) * lo_f32(y.w) + hi_f32(x.w) * hi_f32(y.w);
+  }
+  const float dsum = part + other_half(part);
+  const float dlt = q_ok ? dsum : 0.f;
+  if (sp == 0 && hl == 0 && q_ok) delta[(int64_t)bh * s_pad + qi] = dsum;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     settle(qf[kk]);
@@ -712,18 +703,19 @@ hipError_t fwd_launch(int nb, int s, int nh, int causal, const void *qkv, void *
   return hipSuccess;
 }
 
+// dQ first (it also computes and stores delta), then dK / dV
 template <int D, int OWN>
-hipError_t bwd_launch(int nb, int s, int nh, int causal, const void *qkv, const void *dout, const float *lse,
-                      const float *delta, void *dqkv, hipStream_t st) {
+hipError_t bwd_launch(int nb, int s, int nh, int causal, const void *qkv, const void *o, const void *dout,
+                      const float *lse, float *delta, void *dqkv, hipStream_t st) {
   const float scale = 1.f / sqrtf((float)D);
   const int s_pad = attn_lse_stride(s);
   const bf16_t *q = static_cast<const bf16_t *>(qkv), *d_o = static_cast<const bf16_t *>(dout);
   bf16_t *dq = static_cast<bf16_t *>(dqkv);
   const dim3 grid((s + 32 * OWN - 1) / (32 * OWN), nb * nh);
+  OASES_LAUNCH((attn_dq_kernel<D, OWN>), grid, dim3(64 * NW), st, q, static_cast<const bf16_t *>(o), d_o, lse,
+               delta, dq, s, s_pad, nh, causal, scale * LOG2E, scale);
   OASES_LAUNCH((attn_dkdv_kernel<D, OWN>), grid, dim3(64 * NW), st, q, d_o, lse, delta, dq, s, s_pad, nh,
                causal, scale * LOG2E, scale);
-  OASES_LAUNCH((attn_dq_kernel<D, OWN>), grid, dim3(64 * NW), st, q, d_o, lse, delta, dq, s, s_pad, nh, causal,
-               scale * LOG2E, scale);
   return hipSuccess;
 }
 
@@ -739,14 +731,10 @@ hipError_t fwd_d(int nb, int s, int nh, int causal, const void *qkv, void *o, fl
 template <int D>
 hipError_t bwd_d(int nb, int s, int nh, int causal, const void *qkv, const void *o, const void *dout,
                  const float *lse, float *delta, void *dqkv, hipStream_t st) {
-  const int s_pad = attn_lse_stride(s);
-  const int64_t rows = (int64_t)nb * s * nh;
-  OASES_LAUNCH(attn_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), st,
-               static_cast<const bf16_t *>(o), static_cast<const bf16_t *>(dout), delta, nb, s, s_pad, nh);
   switch (pick_own(s, nb * nh)) {
-    case 4: return bwd_launch<D, 4>(nb, s, nh, causal, qkv, dout, lse, delta, dqkv, st);
-    case 2: return bwd_launch<D, 2>(nb, s, nh, causal, qkv, dout, lse, delta, dqkv, st);
-    default: return bwd_launch<D, 1>(nb, s, nh, causal, qkv, dout, lse, delta, dqkv, st);
+    case 4: return bwd_launch<D, 4>(nb, s, nh, causal, qkv, o, dout, lse, delta, dqkv, st);
+    case 2: return bwd_launch<D, 2>(nb, s, nh, causal, qkv, o, dout, lse, delta, dqkv, st);
+    default: return bwd_launch<D, 1>(nb, s, nh, causal, qkv, o, dout, lse, delta, dqkv, st);
   }
 }
 

@@ -388,7 +388,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   });
 
   // one k tile in LDS slot I (static); stage kt+STAGES-1 goes to slot I+STAGES-1
-  auto step = [&](auto I, int kt) {
+  // (always inlined: an outlined step would keep the accumulators in scratch)
+  auto step = [&](auto I, int kt) __attribute__((always_inline)) {
     using AHEAD = std::integral_constant<int, (decltype(I)::value + STAGES - 1) % STAGES>;
     // this stage's DMA is done once at most the later stages' DMA is outstanding
     wait_vmcnt_upto<STAGES - 2, DL>(min(STAGES - 2, nk - 1 - kt));

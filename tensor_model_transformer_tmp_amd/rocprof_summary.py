@@ -2,7 +2,7 @@
 
 The executor times its kernels in classes (one class launch = one pair of HIP
 events on the launch stream): ``gemm_fwd`` / ``gemm_dx`` / ``gemm_dw`` (one
-GEMM each), ``attn_fwd`` (one kernel), ``attn_bwd`` (delta + dK/dV + dQ
+GEMM each), ``attn_fwd`` (one kernel), ``attn_bwd`` (dQ with delta, then dK/dV
 kernels), ``sum`` (one AllReduce-point sum), ``colsum`` (two passes).  This
 module maps rocprofv3 kernel names onto the same classes so that a kernel
 trace and a counter run can be set beside the event timings.
