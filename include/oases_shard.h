@@ -248,9 +248,13 @@ int oases_sum_grid_cap(int32_t workgroups);
 
 /* Attention work split for this process.  A workgroup has 4 waves of 32
  * rows each; OWN of them own distinct row tiles (sharing each staged block)
- * and 4/OWN split the walk over the other operand.  0 = automatic (the
- * default: the largest OWN that gives 256 workgroups), 1 = OWN 1, 2 = OWN 4,
- * 3 = OWN 2.  For tests and tuning; OASES_E_ARG for other values. */
+ * and 4/OWN split the walk over the other operand.  With tile pairs a
+ * workgroup takes two row tiles, one with a long and one with a short causal
+ * walk.  0 = automatic (the default: the largest OWN that gives 256
+ * workgroups; for the backward, OWN 1 with pairs when pairs alone give 256
+ * workgroups of a causal attention), 1 = OWN 1,
+ * 2 = OWN 4, 3 = OWN 2, 4 = OWN 1 with pairs, 5 = OWN 2 with pairs.  For
+ * tests and tuning; OASES_E_ARG for other values. */
 int oases_attention_variant(int32_t variant);
 
 /* Causal (causal = 1) or full attention forward over QKV [nb*s, 3a]

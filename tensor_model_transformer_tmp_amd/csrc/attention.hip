@@ -15,7 +15,9 @@
 // through LDS in wave order at the end (a fixed order: results are
 // deterministic).  The host picks the largest OWN that still gives 256
 // workgroups, so short sequences with few heads split the walk instead of
-// leaving CUs idle.
+// leaving CUs idle.  Causal walks grow (forward, dQ) or shrink (dK/dV) with
+// the tile index; when there are enough tiles, a backward workgroup takes
+// two, one from each end, so all workgroups carry the same work.
 //
 // Layout of a staged 32 x D block: row-major, 16-byte chunk c of row k at
 // c ^ swz(k).  The swizzle keeps both reads conflict-free on the 64-bank LDS:
@@ -261,7 +263,7 @@ struct KvStager {
 template <int D, int OWN>
 __global__ void __launch_bounds__(64 * NW)
     attn_fwd_kernel(const bf16_t *__restrict__ qkv, bf16_t *__restrict__ out, float *__restrict__ lse,
-                    int s, int s_pad, int nh, int causal, float scale_log2, float scale) {
+                    int s, int s_pad, int nh, int causal, float scale_log2, float scale, int pair) {
   using B = Blk<D>;
   using C = KvCfg<D, OWN>;
   constexpr int SPLIT = C::SPLIT, DL = C::DL;
@@ -270,8 +272,6 @@ __global__ void __launch_bounds__(64 * NW)
   const int l32 = lane & 31, hl = lane >> 5;
   const int own = wave % OWN, sp = wave / OWN;
   const int ntile = (s + 32 * OWN - 1) / (32 * OWN);
-  const int q0 = (ntile - 1 - (int)blockIdx.x) * 32 * OWN;  // heaviest causal tiles first
-  const int qw0 = q0 + own * 32, qi = qw0 + l32;
   const int bh = blockIdx.y, b = bh / nh, h = bh % nh;
   const int a = nh * D, ld = 3 * a;
   const bf16_t *Qp = qkv + (int64_t)b * s * ld + h * D;
@@ -279,6 +279,15 @@ __global__ void __launch_bounds__(64 * NW)
 
   KvStager<D, OWN> stg;
   stg.init(wave, lane, ld, a);
+
+  // tiles of this workgroup, heaviest causal walk first: tile ntile-1-x, and
+  // with pairing also tile x (equal work per workgroup)
+  for (int rep = 0; rep < 1 + pair; ++rep) {
+  const int tile = rep == 0 ? ntile - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  if (rep == 1 && tile >= ntile - 1 - (int)blockIdx.x) break;  // odd count: the middle tile is alone
+  if (rep == 1) lds_barrier();  // the previous tile's combine has read the LDS
+  const int q0 = tile * 32 * OWN;
+  const int qw0 = q0 + own * 32, qi = qw0 + l32;
 
   bf16x8 qf[D / 16];
   {
@@ -388,6 +397,7 @@ __global__ void __launch_bounds__(64 * NW)
         make_uint4(cvt_pk(o[0], o[1]), cvt_pk(o[2], o[3]), cvt_pk(o[4], o[5]), cvt_pk(o[6], o[7]));
     if (d0 == 0) lse[(int64_t)bh * s_pad + qq] = m * scale + logf(L);
   }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -459,7 +469,7 @@ __global__ void __launch_bounds__(64 * NW)
     attn_dkdv_kernel(const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout,
                      const float *__restrict__ lse, const float *__restrict__ delta,
                      bf16_t *__restrict__ dqkv, int s, int s_pad, int nh, int causal, float scale_log2,
-                     float scale) {
+                     float scale, int pair) {
   using B = Blk<D>;
   using C = DkdvCfg<D, OWN>;
   constexpr int SPLIT = C::SPLIT, DL = C::DL;
@@ -467,7 +477,14 @@ __global__ void __launch_bounds__(64 * NW)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int own = wave % OWN, sp = wave / OWN;
-  const int k0 = blockIdx.x * 32 * OWN;  // tile 0 (longest causal walk) first
+  const int ntile = (s + 32 * OWN - 1) / (32 * OWN);
+  // tiles of this workgroup, longest causal walk first: tile x, and with
+  // pairing also tile ntile-1-x
+  for (int rep = 0; rep < 1 + pair; ++rep) {
+  const int tile = rep == 0 ? (int)blockIdx.x : ntile - 1 - (int)blockIdx.x;
+  if (rep == 1 && tile <= (int)blockIdx.x) break;  // odd count: the middle tile is alone
+  if (rep == 1) lds_barrier();  // the previous tile's combine has read the LDS
+  const int k0 = tile * 32 * OWN;
   const int kw0 = k0 + own * 32, kj = kw0 + l32;
   const int bh = blockIdx.y, b = bh / nh, h = bh % nh;
   const int a = nh * D, ld = 3 * a;
@@ -567,6 +584,7 @@ __global__ void __launch_bounds__(64 * NW)
   stash<D>(red + (sp * OWN + own) * D * 32, dk, l32, hl);
   lds_barrier();
   combine_store<D, OWN, SPLIT>(red, dK, ld, k0, s, scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -577,7 +595,7 @@ __global__ void __launch_bounds__(64 * NW)
     attn_dq_kernel(const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ o, const bf16_t *__restrict__ dout,
                    const float *__restrict__ lse, float *__restrict__ delta,
                    bf16_t *__restrict__ dqkv, int s, int s_pad, int nh, int causal, float scale_log2,
-                   float scale) {
+                   float scale, int pair) {
   using B = Blk<D>;
   using C = KvCfg<D, OWN>;  // same staging as the forward: K and V blocks
   constexpr int SPLIT = C::SPLIT, DL = C::DL;
@@ -586,7 +604,12 @@ __global__ void __launch_bounds__(64 * NW)
   const int l32 = lane & 31, hl = lane >> 5;
   const int own = wave % OWN, sp = wave / OWN;
   const int ntile = (s + 32 * OWN - 1) / (32 * OWN);
-  const int q0 = (ntile - 1 - (int)blockIdx.x) * 32 * OWN;
+  // tiles as in the forward: ntile-1-x, and with pairing also x
+  for (int rep = 0; rep < 1 + pair; ++rep) {
+  const int tile = rep == 0 ? ntile - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  if (rep == 1 && tile >= ntile - 1 - (int)blockIdx.x) break;
+  if (rep == 1) lds_barrier();  // the previous tile's combine has read the LDS
+  const int q0 = tile * 32 * OWN;
   const int qw0 = q0 + own * 32, qi = qw0 + l32;
   const int bh = blockIdx.y, b = bh / nh, h = bh % nh;
   const int a = nh * D, ld = 3 * a;
@@ -678,63 +701,92 @@ __global__ void __launch_bounds__(64 * NW)
   stash<D>(red + (sp * OWN + own) * D * 32, dq, l32, hl);
   lds_barrier();
   combine_store<D, OWN, SPLIT>(red, dqkv + (int64_t)b * s * ld + h * D, ld, q0, s, scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-int g_attn_variant = 0;  // 0 = automatic; 1, 2, 3 force OWN = 1, 4, 2 (tests and tuning)
+int g_attn_variant = 0;  // 0 automatic; 1, 2, 3: OWN = 1, 4, 2; 4, 5: OWN = 1, 2 with tile pairs
 
-// waves of a workgroup that own distinct 32-row tiles: the largest that still
-// gives 256 workgroups over all (sequence, head) pairs
-int pick_own(int s, int nbh) {
-  if (g_attn_variant) return g_attn_variant == 1 ? 1 : (g_attn_variant == 2 ? 4 : 2);
+struct AttnPlan {
+  int own;
+  int pair;  // 1: a workgroup takes two tiles, one of the longest and one of the shortest causal walks
+};
+
+// OWN (waves of a workgroup that own distinct 32-row tiles): the largest
+// that still gives 256 workgroups over all (sequence, head) pairs.  Causal
+// walks grow with the tile index; for the backward kernels, when
+// single-owner tiles paired heavy-with-light still give 256 workgroups,
+// every workgroup takes a pair (equal work per workgroup instead of a
+// longest walk twice the average).  The forward keeps shared staging (OWN 2)
+// instead: measured on MI355X, pairs help the backward by up to a fifth at
+// s = 2048 and slow the forward.
+AttnPlan pick_plan(int s, int nbh, int causal, bool bwd) {
+  switch (g_attn_variant) {
+    case 1: return {1, 0};
+    case 2: return {4, 0};
+    case 3: return {2, 0};
+    case 4: return {1, 1};
+    case 5: return {2, 1};
+    default: break;
+  }
+  if (bwd && causal && (int64_t)((s + 31) / 32 / 2) * nbh >= 256) return {1, 1};
   for (int own : {4, 2})
-    if ((int64_t)((s + 32 * own - 1) / (32 * own)) * nbh >= 256) return own;
-  return 1;
+    if ((int64_t)((s + 32 * own - 1) / (32 * own)) * nbh >= 256) return {own, 0};
+  return {1, 0};
+}
+
+// workgroups along a (sequence, head): one per tile, or one per pair of tiles
+int tile_wgs(int s, int own, int pair) {
+  const int ntile = (s + 32 * own - 1) / (32 * own);
+  return pair ? (ntile + 1) / 2 : ntile;
 }
 
 template <int D, int OWN>
-hipError_t fwd_launch(int nb, int s, int nh, int causal, const void *qkv, void *o, float *lse, hipStream_t st) {
+hipError_t fwd_launch(int nb, int s, int nh, int causal, int pair, const void *qkv, void *o, float *lse,
+                      hipStream_t st) {
   const float scale = 1.f / sqrtf((float)D);
-  const dim3 grid((s + 32 * OWN - 1) / (32 * OWN), nb * nh);
+  const dim3 grid(tile_wgs(s, OWN, pair), nb * nh);
   OASES_LAUNCH((attn_fwd_kernel<D, OWN>), grid, dim3(64 * NW), st, static_cast<const bf16_t *>(qkv),
-               static_cast<bf16_t *>(o), lse, s, attn_lse_stride(s), nh, causal, scale * LOG2E, scale);
+               static_cast<bf16_t *>(o), lse, s, attn_lse_stride(s), nh, causal, scale * LOG2E, scale, pair);
   return hipSuccess;
 }
 
 // dQ first (it also computes and stores delta), then dK / dV
 template <int D, int OWN>
-hipError_t bwd_launch(int nb, int s, int nh, int causal, const void *qkv, const void *o, const void *dout,
-                      const float *lse, float *delta, void *dqkv, hipStream_t st) {
+hipError_t bwd_launch(int nb, int s, int nh, int causal, int pair, const void *qkv, const void *o,
+                      const void *dout, const float *lse, float *delta, void *dqkv, hipStream_t st) {
   const float scale = 1.f / sqrtf((float)D);
   const int s_pad = attn_lse_stride(s);
   const bf16_t *q = static_cast<const bf16_t *>(qkv), *d_o = static_cast<const bf16_t *>(dout);
   bf16_t *dq = static_cast<bf16_t *>(dqkv);
-  const dim3 grid((s + 32 * OWN - 1) / (32 * OWN), nb * nh);
+  const dim3 grid(tile_wgs(s, OWN, pair), nb * nh);
   OASES_LAUNCH((attn_dq_kernel<D, OWN>), grid, dim3(64 * NW), st, q, static_cast<const bf16_t *>(o), d_o, lse,
-               delta, dq, s, s_pad, nh, causal, scale * LOG2E, scale);
+               delta, dq, s, s_pad, nh, causal, scale * LOG2E, scale, pair);
   OASES_LAUNCH((attn_dkdv_kernel<D, OWN>), grid, dim3(64 * NW), st, q, d_o, lse, delta, dq, s, s_pad, nh,
-               causal, scale * LOG2E, scale);
+               causal, scale * LOG2E, scale, pair);
   return hipSuccess;
 }
 
 template <int D>
 hipError_t fwd_d(int nb, int s, int nh, int causal, const void *qkv, void *o, float *lse, hipStream_t st) {
-  switch (pick_own(s, nb * nh)) {
-    case 4: return fwd_launch<D, 4>(nb, s, nh, causal, qkv, o, lse, st);
-    case 2: return fwd_launch<D, 2>(nb, s, nh, causal, qkv, o, lse, st);
-    default: return fwd_launch<D, 1>(nb, s, nh, causal, qkv, o, lse, st);
+  const AttnPlan pl = pick_plan(s, nb * nh, causal, false);
+  switch (pl.own) {
+    case 4: return fwd_launch<D, 4>(nb, s, nh, causal, pl.pair, qkv, o, lse, st);
+    case 2: return fwd_launch<D, 2>(nb, s, nh, causal, pl.pair, qkv, o, lse, st);
+    default: return fwd_launch<D, 1>(nb, s, nh, causal, pl.pair, qkv, o, lse, st);
   }
 }
 
 template <int D>
 hipError_t bwd_d(int nb, int s, int nh, int causal, const void *qkv, const void *o, const void *dout,
                  const float *lse, float *delta, void *dqkv, hipStream_t st) {
-  switch (pick_own(s, nb * nh)) {
-    case 4: return bwd_launch<D, 4>(nb, s, nh, causal, qkv, o, dout, lse, delta, dqkv, st);
-    case 2: return bwd_launch<D, 2>(nb, s, nh, causal, qkv, o, dout, lse, delta, dqkv, st);
-    default: return bwd_launch<D, 1>(nb, s, nh, causal, qkv, o, dout, lse, delta, dqkv, st);
+  const AttnPlan pl = pick_plan(s, nb * nh, causal, true);
+  switch (pl.own) {
+    case 4: return bwd_launch<D, 4>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dqkv, st);
+    case 2: return bwd_launch<D, 2>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dqkv, st);
+    default: return bwd_launch<D, 1>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dqkv, st);
   }
 }
 

@@ -770,7 +770,7 @@ int oases_sum_grid_cap(int32_t workgroups) {
 }
 
 int oases_attention_variant(int32_t variant) {
-  if (variant < 0 || variant > 3) return OASES_E_ARG;
+  if (variant < 0 || variant > 5) return OASES_E_ARG;
   attention_set_variant(variant);
   return OASES_OK;
 }

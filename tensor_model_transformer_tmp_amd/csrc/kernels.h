@@ -111,7 +111,7 @@ hipError_t colsum(bool bf16, const void *x, int rows, int cols, int ldx, float *
 
 // Row stride of the lse / delta arrays: s rounded up to 64.
 int attn_lse_stride(int s);
-// 0 automatic, 1 split, 2 query-parallel attention kernels (tests, tuning)
+// 0 automatic; 1, 2, 3: OWN 1, 4, 2; 4, 5: OWN 1, 2 with tile pairs (tests, tuning)
 void attention_set_variant(int v);
 
 // Causal attention over QKV [nb*s, 3a] (columns [Q | K | V], head-major):

@@ -111,12 +111,13 @@ def test_layer_entry_points_match_schedule_step():
     dev.close()
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("name", ["pair_d64_ragged", "pair_d128"])
 def test_attention_variants_full_step(variant, name):
-    """Both attention kernel layouts (split and query-parallel) through the
-    whole step, forward and backward, against the oracle with the shard's own
-    outputs visible (zero peers)."""
+    """Every attention work split (1, 2 or 4 owner waves; single tiles or
+    heavy-with-light tile pairs) through the whole step, forward and
+    backward, against the oracle with the shard's own outputs visible (zero
+    peers)."""
     from tensor_model_transformer_tmp_amd import shard
     cfg = SMALL[name]
     inp = gen.make_inputs(cfg, zero_peers=True)
