@@ -38,6 +38,7 @@ BF16 = 1
 
 # tensor kinds (part of the seed tuple)
 K_X, K_G, K_W_IN, K_B_IN, K_W_OUT, K_PEER_F, K_PEER_B = 1, 2, 10, 11, 12, 20, 21
+K_LN_W, K_LN_B = 13, 14
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,6 +53,11 @@ class ShardConfig:
     ffn_shard      f_s, FFN columns held by this shard
     tmp_width      w, number of TMP ranks summed at an AllReduce point
     dtype          F32 or BF16 (storage type of every activation and weight)
+    full_block     wrap every block in the replicated tail of a transformer
+                   layer: LayerNorm (weights ln_w, ln_b) before the column
+                   GEMM, dropout (drop probability drop_q / 65536, keyed by
+                   drop_seed) and the residual add after the AllReduce point
+    gelu_tanh      FFN GeLU in its tanh form instead of the exact (erf) form
     """
     name: str
     blocks: tuple
@@ -67,6 +73,12 @@ class ShardConfig:
     w_std: float = 0.02
     bias_std: float = 0.0
     seed: int = 20250625
+    full_block: bool = False
+    drop_q: int = 0
+    drop_seed: int = 77
+    ln_eps: float = 1e-5
+    ln_std: float = 0.1
+    gelu_tanh: bool = False
 
     @property
     def n_layers(self) -> int:
@@ -138,14 +150,14 @@ def storage_to_f64(arr: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def draw(cfg: ShardConfig, kind: int, shape, std: float, layer: int = 0, sb: int = 0,
-         k: int = 0) -> np.ndarray:
+         k: int = 0, mean: float = 0.0) -> np.ndarray:
     """One tensor in storage form: float32 array, or uint16 bf16 bit patterns."""
     n = int(np.prod(shape))
     if std == 0.0:
-        v32 = np.zeros(n, np.float32)
+        v32 = np.full(n, mean, np.float32)
     else:
         rng = np.random.default_rng([cfg.seed, kind, layer, sb, k])
-        v32 = (rng.standard_normal(n) * std).astype(np.float32)
+        v32 = (rng.standard_normal(n) * std + mean).astype(np.float32)
     out = _f32_to_bf16_bits(v32) if cfg.dtype == BF16 else v32
     return out.reshape(shape)
 
@@ -161,6 +173,8 @@ class ShardInputs:
     w_out: list
     peers_fwd: np.ndarray   # [L, 2, w-1, T_sb, h]
     peers_bwd: np.ndarray
+    ln_w: list = None       # per layer [h] (full blocks only)
+    ln_b: list = None
 
     def f64(self, name: str, layer: int | None = None) -> np.ndarray:
         v = getattr(self, name)
@@ -201,7 +215,12 @@ def make_inputs(cfg: ShardConfig, zero_peers: bool = False) -> ShardInputs:
             w_in.append(ex.submit(draw, cfg, K_W_IN, (cfg.n_in(l), h), cfg.w_std, l))
             b_in.append(ex.submit(draw, cfg, K_B_IN, (cfg.n_in(l),), cfg.bias_std, l))
             w_out.append(ex.submit(draw, cfg, K_W_OUT, (h, cfg.n_mid(l)), cfg.w_std, l))
+        ln_w = ln_b = None
+        if cfg.full_block:  # LayerNorm weight 1 + N(0, ln_std^2), bias N(0, ln_std^2)
+            ln_w = [ex.submit(draw, cfg, K_LN_W, (h,), cfg.ln_std, l, 0, 0, 1.0) for l in range(L)]
+            ln_b = [ex.submit(draw, cfg, K_LN_B, (h,), cfg.ln_std, l) for l in range(L)]
+            ln_w, ln_b = [f.result() for f in ln_w], [f.result() for f in ln_b]
         return ShardInputs(cfg=cfg, x=fx.result(), g=fg.result(),
                            w_in=[f.result() for f in w_in], b_in=[f.result() for f in b_in],
                            w_out=[f.result() for f in w_out],
-                           peers_fwd=peers[K_PEER_F], peers_bwd=peers[K_PEER_B])
+                           peers_fwd=peers[K_PEER_F], peers_bwd=peers[K_PEER_B], ln_w=ln_w, ln_b=ln_b)

@@ -16,7 +16,12 @@ Source: Oases (arXiv 2305.16121), Section IV:
 
 Reading used here: a block l is "F_l = column GEMM -> GeLU | attention -> row
 GEMM, C_l = AllReduce of the row GEMM's partial".  The replicated tail F_j is
-empty (no LayerNorm / residual on this path), so block l+1 plays F_j.  The
+empty (no LayerNorm / residual on this path), so block l+1 plays F_j.  With
+``full_block`` configurations F_j is the tail of a transformer layer, the
+same on every rank: dropout and the residual add right after the AllReduce
+point, then the next block's LayerNorm before its column GEMM.  C_l(F) then
+yields r_{l+1} = r_l + dropout(sum), and the backward runs the LayerNorm
+backward and the residual add right after C_l(B).  The
 backward of block l is split into B_dX (the data-gradient path that feeds
 C_l(B)) and B_dW (weight gradients), and C_l(B) is started before B_dW.
 
@@ -89,6 +94,9 @@ def run_step(inp, mode: str, keep_trace: bool = False, keep_dy: bool = False):
     w_in = [inp.f64("w_in", l) for l in range(L)]
     b_in = [inp.f64("b_in", l) for l in range(L)]
     w_out = [inp.f64("w_out", l) for l in range(L)]
+    full = cfg.full_block
+    ln_w = [inp.f64("ln_w", l) for l in range(L)] if full else None
+    ln_b = [inp.f64("ln_b", l) for l in range(L)] if full else None
 
     def peers(kind, l, sb):
         src = inp.peers_fwd if kind == "fwd" else inp.peers_bwd
@@ -105,10 +113,18 @@ def run_step(inp, mode: str, keep_trace: bool = False, keep_dy: bool = False):
     trace = []
     fwd_sums = {}
 
+    def gemm_in(l, sb):
+        """The column GEMM's input: the block input, or its LayerNorm."""
+        x = mem.get_(("X", l, sb))
+        return blocks.layer_norm(x, ln_w[l], ln_b[l], cfg.ln_eps) if full else x
+
     def fwd(l, sb):
         kind = cfg.blocks[l]
-        return blocks.block_forward(kind, mem.get_(("X", l, sb)), w_in[l], b_in[l], w_out[l],
-                                    nb, s, nh, d, cfg.causal)
+        return blocks.block_forward(kind, gemm_in(l, sb), w_in[l], b_in[l], w_out[l],
+                                    nb, s, nh, d, cfg.causal, cfg.gelu_tanh)
+
+    def keep(l, sb):
+        return blocks.dropout_keep(T, cfg.hidden, l, sb, cfg.drop_seed, cfg.drop_q)
 
     for op in build_ops(L, mode):
         kind, l, sb, _ = op
@@ -121,6 +137,8 @@ def run_step(inp, mode: str, keep_trace: bool = False, keep_dy: bool = False):
                 mem[("act", l, sb)] = acts
         elif kind == "C_F":
             y = blocks.allreduce_point(mem.pop(("P", l, sb)), peers("fwd", l, sb))
+            if full:
+                y = blocks.dropout_residual(mem.get_(("X", l, sb)), y, keep(l, sb), cfg.drop_q)
             mem[("X", l + 1, sb) if l + 1 < L else ("Y", sb)] = y
             fwd_sums[(l, sb)] = y  # kept outside the store, only to check C_R
             if l == L - 1 and sb == 1:
@@ -132,17 +150,25 @@ def run_step(inp, mode: str, keep_trace: bool = False, keep_dy: bool = False):
                 mem[("P_R", l, sb)] = p
         elif kind == "C_R":
             y = blocks.allreduce_point(mem.pop(("P_R", l, sb)), peers("fwd", l, sb))
+            if full:
+                y = blocks.dropout_residual(mem.get_(("X", l, sb)), y, keep(l, sb), cfg.drop_q)
             if not np.array_equal(y, fwd_sums[(l, sb)]):
                 raise AssertionError("recomputed AllReduce differs from the forward one")
         elif kind == "B_dX":
             blk = cfg.blocks[l]
-            dxo, g = blocks.block_backward(blk, mem.get_(("X", l, sb)), mem.get_(("act", l, sb)),
-                                           mem.get_(("dY", l, sb)), w_in[l], w_out[l],
-                                           nb, s, nh, d)
+            dy = mem.get_(("dY", l, sb))
+            # dropout backward: the AllReduce inputs' gradient (Eq. (1))
+            dp = np.where(keep(l, sb), dy * (65536.0 / (65536 - cfg.drop_q)), 0.0) if full else dy
+            dxo, g = blocks.block_backward(blk, gemm_in(l, sb), mem.get_(("act", l, sb)),
+                                           dp, w_in[l], w_out[l], nb, s, nh, d, cfg.gelu_tanh)
             mem[("dXown", l, sb)] = dxo
             mem[("wgrad", l, sb)] = g
         elif kind == "C_B":
             dx = blocks.allreduce_point(mem.pop(("dXown", l, sb)), peers("bwd", l, sb))
+            if full:  # LayerNorm backward and the residual path, after the sum
+                dxl, dlw, dlb = blocks.layer_norm_backward(mem.get_(("X", l, sb)), ln_w[l], cfg.ln_eps, dx)
+                dx = mem.get_(("dY", l, sb)) + dxl
+                mem.get_(("wgrad", l, sb)).update({"dln_w": dlw, "dln_b": dlb})
             mem[("dY", l - 1, sb) if l > 0 else ("dX", sb)] = dx
             if keep_dy and l > 0:
                 dys[(l - 1, sb)] = dx
@@ -179,17 +205,34 @@ def run_unsplit(inp):
         return [np.concatenate([storage_to_f64(src[l, sb, k], cfg.dtype) for sb in (0, 1)])
                 for k in range(cfg.tmp_width - 1)]
 
+    full, T, h = cfg.full_block, cfg.t_sb, cfg.hidden
+    scale = 65536.0 / (65536 - cfg.drop_q)
+
+    def keep_full(l):  # masks are drawn per sub-batch (sub-batch counters)
+        return np.concatenate([blocks.dropout_keep(T, h, l, sb, cfg.drop_seed, cfg.drop_q) for sb in (0, 1)])
+
+    def gemm_in(l, x):
+        return blocks.layer_norm(x, inp.f64("ln_w", l), inp.f64("ln_b", l), cfg.ln_eps) if full else x
+
     xs, acts = [inp.f64("x")], []
     for l in range(L):
-        p, a = blocks.block_forward(cfg.blocks[l], xs[-1], inp.f64("w_in", l), inp.f64("b_in", l),
-                                    inp.f64("w_out", l), nb, s, nh, d, cfg.causal)
+        p, a = blocks.block_forward(cfg.blocks[l], gemm_in(l, xs[-1]), inp.f64("w_in", l), inp.f64("b_in", l),
+                                    inp.f64("w_out", l), nb, s, nh, d, cfg.causal, cfg.gelu_tanh)
         acts.append(a)
-        xs.append(blocks.allreduce_point(p, peers_full(inp.peers_fwd, l)))
+        y = blocks.allreduce_point(p, peers_full(inp.peers_fwd, l))
+        xs.append(blocks.dropout_residual(xs[-1], y, keep_full(l), cfg.drop_q) if full else y)
     dy = inp.f64("g")
     grads = [None] * L
     for l in reversed(range(L)):
-        dxo, grads[l] = blocks.block_backward(cfg.blocks[l], xs[l], acts[l], dy,
+        dp = np.where(keep_full(l), dy * scale, 0.0) if full else dy
+        dxo, grads[l] = blocks.block_backward(cfg.blocks[l], gemm_in(l, xs[l]), acts[l], dp,
                                               inp.f64("w_in", l), inp.f64("w_out", l),
-                                              nb, s, nh, d)
-        dy = blocks.allreduce_point(dxo, peers_full(inp.peers_bwd, l))
+                                              nb, s, nh, d, cfg.gelu_tanh)
+        dz = blocks.allreduce_point(dxo, peers_full(inp.peers_bwd, l))
+        if full:
+            dxl, grads[l]["dln_w"], grads[l]["dln_b"] = blocks.layer_norm_backward(
+                xs[l], inp.f64("ln_w", l), cfg.ln_eps, dz)
+            dy = dy + dxl
+        else:
+            dy = dz
     return {"Y": xs[-1], "dX": dy, "grads": grads}

@@ -186,9 +186,12 @@ def _f64_inputs(cfg, zero_bwd_peers=True):
     inp = gen.make_inputs(cfg)
     f = lambda a: a.astype(np.float64)
     pb = np.zeros_like(f(inp.peers_bwd)) if zero_bwd_peers else f(inp.peers_bwd)
+    ln = {}
+    if cfg.full_block:
+        ln = dict(ln_w=[f(a) for a in inp.ln_w], ln_b=[f(a) for a in inp.ln_b])
     return dataclasses.replace(inp, x=f(inp.x), g=f(inp.g), w_in=[f(a) for a in inp.w_in],
                                b_in=[f(a) for a in inp.b_in], w_out=[f(a) for a in inp.w_out],
-                               peers_fwd=f(inp.peers_fwd), peers_bwd=pb)
+                               peers_fwd=f(inp.peers_fwd), peers_bwd=pb, **ln)
 
 
 def _step_loss(inp):
@@ -358,3 +361,130 @@ def test_sum_bf16_round_to_nearest_even():
     assert sums.allreduce_point_storage(odd, [half_ulp, zero], True)[0] == 0x3F82
     neg = np.array([0xBF80], np.uint16)          # -1 + 1 = +0
     assert sums.allreduce_point_storage(neg, [one], True)[0] == 0x0000
+
+
+# ----------------------------------------------------------------------------
+# full transformer block: LayerNorm, dropout (Philox4x64-10), residual, tanh GeLU
+# ----------------------------------------------------------------------------
+
+def test_philox_matches_numpy_bit_generator():
+    """The oracle's Philox4x64-10 (written from the SC'11 definition) against
+    numpy's Philox bit generator, which advances its 4-word counter (with
+    carry) before producing each block of four words."""
+    M = (1 << 64) - 1
+    for key in ((0, 0), (123, 456), (M, 7)):
+        for ctr in ((0, 0, 0, 0), (5, 1, 2, 3), (M - 1, 9, 0, 1)):
+            bg = np.random.Philox(key=np.array(key, np.uint64), counter=np.array(ctr, np.uint64))
+            raw = bg.random_raw(8)
+            c = list(ctr)
+            got = []
+            for _ in range(2):
+                for i in range(4):  # increment with carry
+                    c[i] = (c[i] + 1) & M
+                    if c[i]:
+                        break
+                got += [int(w) for w in blocks.philox4x64(*[np.uint64(v) for v in c], *key)]
+            assert got == [int(v) for v in raw], (key, ctr)
+
+
+def test_dropout_mask_rate_and_layout():
+    T, h = 64, 96
+    assert blocks.dropout_keep(T, h, 0, 0, 5, 0).all()
+    keep = blocks.dropout_keep(T, h, 1, 0, 5, 16384)  # p = 1/4
+    n = keep.size
+    assert abs(keep.sum() - 0.75 * n) < 5 * math.sqrt(n * 0.75 * 0.25)
+    # element e = row*h + col is word e % 4 of counter e // 4 (sub-batch in word 1, layer in the key)
+    for (r, c) in ((0, 0), (3, 7), (T - 1, h - 1)):
+        e = r * h + c
+        w = blocks.philox4x64(np.uint64(e // 4), np.uint64(0), np.uint64(0), np.uint64(0), 5, 1)[e % 4]
+        assert keep[r, c] == (int(w) < (65536 - 16384) << 48)
+    # sub-batches and layers draw different masks
+    assert (keep != blocks.dropout_keep(T, h, 1, 1, 5, 16384)).any()
+    assert (keep != blocks.dropout_keep(T, h, 2, 0, 5, 16384)).any()
+
+
+def test_layer_norm_matches_torch():
+    import torch
+    x, w, b = RNG.standard_normal((7, 24)) * 3 + 1, RNG.standard_normal(24), RNG.standard_normal(24)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (24,), torch.from_numpy(w),
+                                         torch.from_numpy(b), 1e-5).numpy()
+    np.testing.assert_allclose(blocks.layer_norm(x, w, b, 1e-5), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_norm_backward_matches_autograd():
+    import torch
+    x, w, b = RNG.standard_normal((5, 16)) * 2, RNG.standard_normal(16), RNG.standard_normal(16)
+    dz = RNG.standard_normal((5, 16))
+    tx, tw, tb = (torch.tensor(v, requires_grad=True) for v in (x, w, b))
+    torch.nn.functional.layer_norm(tx, (16,), tw, tb, 1e-5).backward(torch.from_numpy(dz))
+    dx, dw, db = blocks.layer_norm_backward(x, w, 1e-5, dz)
+    for got, want in ((dx, tx.grad), (dw, tw.grad), (db, tb.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_gelu_tanh_matches_torch():
+    import torch
+    u = np.linspace(-6, 6, 241)
+    tu = torch.tensor(u, requires_grad=True)
+    y = torch.nn.functional.gelu(tu, approximate="tanh")
+    y.backward(torch.ones_like(tu))
+    np.testing.assert_allclose(blocks.gelu_tanh(u), y.detach().numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(blocks.gelu_tanh_grad(u), tu.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def _full_cfg(**kw):
+    return _tiny_cfg(full_block=True, drop_q=13107, drop_seed=11, ln_std=0.3, **kw)
+
+
+@pytest.mark.parametrize("tanh", [False, True])
+def test_full_block_step_directional_finite_difference(tanh):
+    """Full blocks (LayerNorm, dropout, residual): <grad, v> equals the
+    directional derivative of L = <Y_top, G> over the input, every weight and
+    the LayerNorm weights (the dropout mask is fixed by its counters)."""
+    cfg = _full_cfg(gelu_tanh=tanh)
+    inp = _f64_inputs(cfg)
+    params = [("x", None)] + [(n, l) for l in range(cfg.n_layers)
+                              for n in ("w_in", "b_in", "w_out", "ln_w", "ln_b")]
+    gname = {"w_in": "dw_in", "b_in": "db_in", "w_out": "dw_out", "ln_w": "dln_w", "ln_b": "dln_b"}
+
+    def get(i, name, l):
+        return getattr(i, name) if l is None else getattr(i, name)[l]
+
+    dirs = {p: RNG.standard_normal(get(inp, *p).shape) for p in params}
+    for mode in schedule.MODES:
+        out = schedule.run_step(inp, mode)
+        analytic = np.sum(out["dX"] * dirs[("x", None)])
+        for (n, l), dvec in dirs.items():
+            if l is not None:
+                analytic += np.sum(out["grads"][l][gname[n]] * dvec)
+        eps = 1e-6
+        vals = []
+        for sgn in (1, -1):
+            pert = _f64_inputs(cfg)
+            for (n, l), dvec in dirs.items():
+                get(pert, n, l)[...] += sgn * eps * dvec
+            vals.append(_step_loss(pert))
+        fd = (vals[0] - vals[1]) / (2 * eps)
+        assert analytic == pytest.approx(fd, rel=1e-7), mode
+
+
+def test_full_block_schedules_identical_and_residual():
+    """All schedules agree bit for bit and match the unsplit reference; with
+    zero forward peers and all-zero block weights a full block is the
+    identity on the residual stream."""
+    cfg = _full_cfg(blocks_=(gen.ATTN, gen.FFN, gen.FFN))
+    inp = _f64_inputs(cfg, zero_bwd_peers=False)
+    ref = schedule.run_step(inp, "serial_norecompute")
+    for mode in schedule.MODES:
+        out = schedule.run_step(inp, mode)
+        np.testing.assert_array_equal(out["Y"], ref["Y"])
+        np.testing.assert_array_equal(out["dX"], ref["dX"])
+    unsplit = schedule.run_unsplit(inp)
+    np.testing.assert_allclose(ref["Y"], unsplit["Y"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(ref["dX"], unsplit["dX"], rtol=1e-12, atol=1e-12)
+    for l in range(cfg.n_layers):
+        for n in ("dw_in", "db_in", "dw_out", "dln_w", "dln_b"):
+            np.testing.assert_allclose(ref["grads"][l][n], unsplit["grads"][l][n], rtol=1e-12, atol=1e-12)
+    z = dataclasses.replace(inp, w_out=[np.zeros_like(w) for w in inp.w_out],
+                            peers_fwd=np.zeros_like(inp.peers_fwd))
+    np.testing.assert_allclose(schedule.run_step(z, "serial_fine")["Y"], inp.x, rtol=0, atol=1e-15)
