@@ -97,7 +97,18 @@ typedef enum {
  *   hidden, ffn_shard multiples of 64; tmp_width >= 1;
  *   attention blocks: head_dim in {64, 128}, heads_per_shard >= 1,
  *   and dtype OASES_BF16 (float32 attention is OASES_E_UNSUPPORTED);
- *   causal in {0, 1}.  The blocks array is copied by oases_create. */
+ *   causal in {0, 1}.  The blocks array is copied by oases_create.
+ * Full transformer block (the replicated tail F_j of Section IV; bf16 only,
+ * OASES_E_UNSUPPORTED for float32): with full_block = 1 every block's column
+ * GEMM reads LayerNorm(x) (weights ln_w, ln_b, epsilon ln_eps > 0; biased
+ * variance) instead of its input x, and its AllReduce point yields
+ * x + dropout(sum) instead of the sum.  Dropout drops each element with
+ * probability drop_q / 65536 (drop_q in [0, 65535]): element e of a
+ * sub-batch's [T_sb, h] tensor is kept iff word e % 4 of Philox4x64-10 at
+ * counter (e / 4, sub_batch, 0, 0) under key (drop_seed, layer) is below
+ * (65536 - drop_q) * 2^48, and kept elements are scaled by
+ * 65536 / (65536 - drop_q).  gelu_tanh = 1 uses the tanh form of GeLU in the
+ * FFN blocks (bf16 only). */
 typedef struct {
   int32_t n_layers;
   const int32_t *blocks;
@@ -105,15 +116,24 @@ typedef struct {
   int32_t heads_per_shard, head_dim, ffn_shard, tmp_width;
   int32_t dtype;   /* oases_dtype */
   int32_t causal;
+  int32_t full_block;  /* 0: bare blocks; 1: LayerNorm / dropout / residual */
+  int32_t drop_q;
+  uint64_t drop_seed;
+  float ln_eps;
+  int32_t gelu_tanh;
 } oases_config;
 
 /* Per-layer parameters.  N_in = 3a (attention) or f_s (FFN); N_mid = a or f_s.
  *   w_in [N_in, h], b_in [N_in], w_out [h, N_mid]           storage type
  *   dw_in [N_in, h], db_in [N_in], dw_out [h, N_mid]         float32, written
- *   (overwritten by sub-batch 0, accumulated by sub-batch 1 of each step). */
+ *   (overwritten by sub-batch 0, accumulated by sub-batch 1 of each step).
+ *   ln_w, ln_b [h] (storage type) and dln_w, dln_b [h] (float32, written the
+ *   same way): the LayerNorm of full blocks; NULL otherwise. */
 typedef struct {
   const void *w_in, *b_in, *w_out;
   void *dw_in, *db_in, *dw_out;
+  const void *ln_w, *ln_b;
+  void *dln_w, *dln_b;
 } oases_layer_params;
 
 /* Activation buffers (storage type unless stated):
@@ -223,9 +243,11 @@ int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int
  *            4: C (float32) = acc, plus the old C when beta != 0;
  *            5 (bfloat16 only): as 4, and pre (float32, m elements) = the sums of
  *            A(m, k) over k, plus the old pre when beta != 0 (a bias gradient
- *            taken beside its weight gradient).
- * Supported: layouts (0,0) with epilogues 0-2 (forward / recompute), (0,1) with
- * 0 and 3 (data gradient), (1,1) with 4 and 5 (weight gradient).  Storage-type
+ *            taken beside its weight gradient); 6, 7 (bfloat16 only): as 2 and 3
+ *            with the tanh form of GeLU.
+ * Supported: layouts (0,0) with epilogues 0-2 and 6 (forward / recompute),
+ * (0,1) with 0, 3 and 7 (data gradient), (1,1) with 4 and 5 (weight
+ * gradient).  Storage-type
  * operands; the contiguous dimension of every operand and N are multiples of
  * 8; leading dimensions in elements, multiples of 8.  pre and C (epilogues
  * 0-3) use ldc; aux uses ld_aux. */

@@ -29,6 +29,51 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 64x64 -> 128-bit products on the 4-word counter, key bumped by the Weyl
+// constants after each round.  The counter is replaced by the output.
+__device__ __forceinline__ void philox4x64(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+// Dropout + residual of the 8 elements of vector v (elements 8v .. 8v+7 of a
+// sub-batch buffer): acc[e] = res[e] + (kept ? acc[e] * scale : 0), one fused
+// multiply-add, so every kernel that applies it gets the same bits.
+__device__ __forceinline__ void drop_res8(float (&acc)[8], uint4 res, int64_t v, uint64_t seed,
+                                          uint64_t layer, uint64_t sb, uint64_t thr, float scale,
+                                          bool drop) {
+  const float r[8] = {lo_f32(res.x), hi_f32(res.x), lo_f32(res.y), hi_f32(res.y),
+                      lo_f32(res.z), hi_f32(res.z), lo_f32(res.w), hi_f32(res.w)};
+  if (!drop) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(acc[e], 1.f, r[e]);
+    return;
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    uint64_t c[4] = {(uint64_t)(2 * v + hh), sb, 0ull, 0ull};
+    philox4x64(c, seed, layer);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * hh + j;
+      acc[e] = c[j] < thr ? __builtin_fmaf(acc[e], scale, r[e]) : r[e];
+    }
+  }
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
@@ -162,6 +207,23 @@ __device__ __forceinline__ float gelu_f(float u) { return u * normal_cdf_pdf(u).
 __device__ __forceinline__ float gelu_grad_f(float u) {
   const PhiParts p = normal_cdf_pdf(u);
   return fmaf(u, p.pdf, p.phi_cdf);
+}
+
+// GeLU, tanh form: gelu_t(u) = u/2 (1 + tanh(k)), k = sqrt(2/pi) (u + 0.044715 u^3);
+// d/du = (1 + tanh k)/2 + u/2 (1 - tanh^2 k) sqrt(2/pi) (1 + 3 * 0.044715 u^2).
+// tanh k = 1 - 2 / (1 + e^(2k)) with e^(2k) = 2^(2k log2 e) (v_exp_f32); the
+// form saturates to +-1 for large |k| (e^(2k) -> inf or 0).
+__device__ __forceinline__ float tanh_of(float k) {
+  return 1.f - 2.f / (1.f + __builtin_amdgcn_exp2f(k * 2.8853900817779268f));  // 2 log2(e)
+}
+__device__ __forceinline__ float gelu_tanh_f(float u) {
+  const float k = 0.7978845608028654f * fmaf(0.044715f * u, u * u, u);
+  return 0.5f * u * (1.f + tanh_of(k));
+}
+__device__ __forceinline__ float gelu_tanh_grad_f(float u) {
+  const float k = 0.7978845608028654f * fmaf(0.044715f * u, u * u, u);
+  const float t = tanh_of(k);
+  return 0.5f * (1.f + t) + 0.5f * u * (1.f - t * t) * 0.7978845608028654f * fmaf(0.134145f * u, u, 1.f);
 }
 
 }  // namespace oases

@@ -37,7 +37,7 @@ __device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
 template <int NP>
 __global__ void __launch_bounds__(SUM_NT)
     allreduce_bf16_kernel(const uint4 *__restrict__ own, const bf16_t *__restrict__ peers,
-                          int64_t peer_stride, uint4 *__restrict__ out, int64_t nvec) {
+                          int64_t peer_stride, uint4 *__restrict__ out, int64_t nvec, DropRes t) {
   constexpr int UNROLL = NP >= 4 ? 2 : 4;
   const int64_t stride = (int64_t)gridDim.x * SUM_NT;
   for (int64_t v0 = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v0 < nvec; v0 += stride * UNROLL) {
@@ -63,6 +63,9 @@ __global__ void __launch_bounds__(SUM_NT)
         acc[0] += lo_f32(b.x); acc[1] += hi_f32(b.x); acc[2] += lo_f32(b.y); acc[3] += hi_f32(b.y);
         acc[4] += lo_f32(b.z); acc[5] += hi_f32(b.z); acc[6] += lo_f32(b.w); acc[7] += hi_f32(b.w);
       }
+      if (t.res)
+        drop_res8(acc, reinterpret_cast<const uint4 *>(t.res)[v], v, t.seed, t.layer, t.sb, t.thr, t.scale,
+                  t.drop);
       out[v] = make_uint4(cvt_pk(acc[0], acc[1]), cvt_pk(acc[2], acc[3]), cvt_pk(acc[4], acc[5]),
                           cvt_pk(acc[6], acc[7]));
     }
@@ -72,7 +75,8 @@ __global__ void __launch_bounds__(SUM_NT)
 // more peers than the unrolled kernels cover: a runtime loop over the peers
 __global__ void __launch_bounds__(SUM_NT)
     allreduce_bf16_many_kernel(const uint4 *__restrict__ own, const bf16_t *__restrict__ peers,
-                               int64_t peer_stride, int n_peers, uint4 *__restrict__ out, int64_t nvec) {
+                               int64_t peer_stride, int n_peers, uint4 *__restrict__ out, int64_t nvec,
+                               DropRes t) {
   for (int64_t v = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * SUM_NT) {
     const uint4 a = stream_load(own + v);
     float acc[8] = {lo_f32(a.x), hi_f32(a.x), lo_f32(a.y), hi_f32(a.y),
@@ -82,6 +86,8 @@ __global__ void __launch_bounds__(SUM_NT)
       acc[0] += lo_f32(b.x); acc[1] += hi_f32(b.x); acc[2] += lo_f32(b.y); acc[3] += hi_f32(b.y);
       acc[4] += lo_f32(b.z); acc[5] += hi_f32(b.z); acc[6] += lo_f32(b.w); acc[7] += hi_f32(b.w);
     }
+    if (t.res)
+      drop_res8(acc, reinterpret_cast<const uint4 *>(t.res)[v], v, t.seed, t.layer, t.sb, t.thr, t.scale, t.drop);
     out[v] = make_uint4(cvt_pk(acc[0], acc[1]), cvt_pk(acc[2], acc[3]), cvt_pk(acc[4], acc[5]),
                         cvt_pk(acc[6], acc[7]));
   }
@@ -169,13 +175,183 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Full transformer block (bf16): LayerNorm forward / backward, dropout
+// backward.  A row of h elements belongs to one wave (64 lanes x 16-byte
+// vectors); row statistics are wave reductions in a fixed butterfly order.
+// The mean and the biased variance are two passes over the row, so
+// var = mean((x - mean)^2) exactly as defined.
+// ---------------------------------------------------------------------------
+constexpr int LN_ROWS = 4;  // rows (waves) per workgroup
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(const uint4 a, float (&f)[8]) {
+  f[0] = lo_f32(a.x); f[1] = hi_f32(a.x); f[2] = lo_f32(a.y); f[3] = hi_f32(a.y);
+  f[4] = lo_f32(a.z); f[5] = hi_f32(a.z); f[6] = lo_f32(a.w); f[7] = hi_f32(a.w);
+}
+
+// mean and 1/sqrt(var + eps) of a row of hv 8-element vectors
+__device__ __forceinline__ void row_stats(const uint4 *xr, int hv, int lane, float eps, float &mu, float &rstd) {
+  const float inv_h = 1.f / (float)(hv * 8);
+  float sum = 0.f;
+  for (int j = lane; j < hv; j += 64) {
+    float f[8];
+    unpack8(xr[j], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += f[e];
+  }
+  mu = wave_sum(sum) * inv_h;
+  float sq = 0.f;
+  for (int j = lane; j < hv; j += 64) {
+    float f[8];
+    unpack8(xr[j], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float dlt = f[e] - mu;
+      sq += dlt * dlt;
+    }
+  }
+  rstd = rsqrtf(wave_sum(sq) * inv_h + eps);
+}
+
+__global__ void __launch_bounds__(64 * LN_ROWS)
+    ln_fwd_kernel(const uint4 *__restrict__ x, const uint4 *__restrict__ w, const uint4 *__restrict__ b,
+                  uint4 *__restrict__ z, int rows, int hv, float eps) {
+  const int row = blockIdx.x * LN_ROWS + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const uint4 *xr = x + (int64_t)row * hv;
+  float mu, rstd;
+  row_stats(xr, hv, lane, eps, mu, rstd);
+  for (int j = lane; j < hv; j += 64) {
+    float f[8], gw[8], gb[8];
+    unpack8(xr[j], f);
+    unpack8(w[j], gw);
+    unpack8(b[j], gb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf((f[e] - mu) * rstd, gw[e], gb[e]);
+    z[(int64_t)row * hv + j] = make_uint4(cvt_pk(f[0], f[1]), cvt_pk(f[2], f[3]), cvt_pk(f[4], f[5]),
+                                          cvt_pk(f[6], f[7]));
+  }
+}
+
+// dx = g + rstd * (w dz - mean(w dz) - xhat * mean(w dz xhat)); stats[row] = (mean, rstd)
+__global__ void __launch_bounds__(64 * LN_ROWS)
+    ln_bwd_kernel(const uint4 *__restrict__ dz, const uint4 *__restrict__ x, const uint4 *__restrict__ w,
+                  const uint4 *__restrict__ g, uint4 *__restrict__ dx, float2 *__restrict__ stats, int rows,
+                  int hv, float eps) {
+  const int row = blockIdx.x * LN_ROWS + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t base = (int64_t)row * hv;
+  float mu, rstd;
+  row_stats(x + base, hv, lane, eps, mu, rstd);
+  float s1 = 0.f, s2 = 0.f;
+  for (int j = lane; j < hv; j += 64) {
+    float fx[8], fd[8], fw[8];
+    unpack8(x[base + j], fx);
+    unpack8(dz[base + j], fd);
+    unpack8(w[j], fw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gy = fw[e] * fd[e];
+      s1 += gy;
+      s2 += gy * ((fx[e] - mu) * rstd);
+    }
+  }
+  const float inv_h = 1.f / (float)(hv * 8);
+  const float m1 = wave_sum(s1) * inv_h, m2 = wave_sum(s2) * inv_h;
+  for (int j = lane; j < hv; j += 64) {
+    float fx[8], fd[8], fw[8], fg[8], o[8];
+    unpack8(x[base + j], fx);
+    unpack8(dz[base + j], fd);
+    unpack8(w[j], fw);
+    unpack8(g[base + j], fg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xh = (fx[e] - mu) * rstd;
+      o[e] = fg[e] + rstd * (fw[e] * fd[e] - m1 - xh * m2);
+    }
+    dx[base + j] = make_uint4(cvt_pk(o[0], o[1]), cvt_pk(o[2], o[3]), cvt_pk(o[4], o[5]), cvt_pk(o[6], o[7]));
+  }
+  if (lane == 0) stats[row] = make_float2(mu, rstd);
+}
+
+// column partials of dw = sum_rows dz * xhat and db = sum_rows dz over chunks of
+// CS_ROWS rows, in the layout and fixed order of colsum_pass1 (partial_w and
+// partial_b each [chunks][h])
+__global__ void __launch_bounds__(256)
+    ln_grad_pass1(const bf16_t *__restrict__ dz, const bf16_t *__restrict__ x, const float2 *__restrict__ stats,
+                  int rows, int h, float *__restrict__ partial_w, float *__restrict__ partial_b) {
+  __shared__ float sw[8][257], sb[8][257];
+  const int cg = threadIdx.x & 31, rl = threadIdx.x >> 5;
+  const int c8 = blockIdx.x * 256 + cg * 8;
+  const int r0 = blockIdx.y * CS_ROWS;
+  float aw[8] = {}, ab[8] = {};
+  if (c8 < h) {
+    for (int i = 0; i < CS_ROWS / 8; ++i) {
+      const int r = r0 + rl + 8 * i;
+      if (r >= rows) break;
+      const float2 st = stats[r];
+      float fd[8], fx[8];
+      unpack8(*reinterpret_cast<const uint4 *>(dz + (int64_t)r * h + c8), fd);
+      unpack8(*reinterpret_cast<const uint4 *>(x + (int64_t)r * h + c8), fx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        aw[e] += fd[e] * ((fx[e] - st.x) * st.y);
+        ab[e] += fd[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sw[rl][cg * 8 + e] = aw[e];
+    sb[rl][cg * 8 + e] = ab[e];
+  }
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < h) {
+    float tw = sw[0][threadIdx.x], tb = sb[0][threadIdx.x];
+#pragma unroll
+    for (int l = 1; l < 8; ++l) {
+      tw += sw[l][threadIdx.x];
+      tb += sb[l][threadIdx.x];
+    }
+    partial_w[(int64_t)blockIdx.y * h + c] = tw;
+    partial_b[(int64_t)blockIdx.y * h + c] = tb;
+  }
+}
+
+__global__ void __launch_bounds__(SUM_NT)
+    dropout_bwd_kernel(const uint4 *__restrict__ g, uint4 *__restrict__ out, int64_t nvec, DropRes t) {
+  for (int64_t v = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * SUM_NT) {
+    float f[8];
+    unpack8(g[v], f);
+    if (t.drop) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint64_t c[4] = {(uint64_t)(2 * v + hh), t.sb, 0ull, 0ull};
+        philox4x64(c, t.seed, t.layer);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[4 * hh + j] = c[j] < t.thr ? f[4 * hh + j] * t.scale : 0.f;
+      }
+    }
+    out[v] = make_uint4(cvt_pk(f[0], f[1]), cvt_pk(f[2], f[3]), cvt_pk(f[4], f[5]), cvt_pk(f[6], f[7]));
+  }
+}
+
 }  // namespace
 
 int g_sum_grid_cap = 512;  // workgroups of the AllReduce-point sum (tunable)
 
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
-                           int n_peers, void *out, int64_t n, hipStream_t s) {
+                           int n_peers, void *out, int64_t n, hipStream_t s, const DropRes *tail) {
   if (n <= 0) return hipSuccess;
+  if (tail && tail->res && !bf16) return hipErrorInvalidValue;
+  const DropRes t = tail ? *tail : DropRes{};
   const int64_t per_vec = bf16 ? 8 : 4;
   const int64_t nvec = n / per_vec;
   const int unroll = bf16 && n_peers <= 7 ? (n_peers >= 4 ? 2 : 4) : 1;
@@ -191,12 +367,12 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
   }
   switch (n_peers) {
 #define OASES_SUM_CASE(NP) \
-  case NP: OASES_LAUNCH(allreduce_bf16_kernel<NP>, grid, dim3(SUM_NT), s, o, p, peer_stride, y, nvec); break;
+  case NP: OASES_LAUNCH(allreduce_bf16_kernel<NP>, grid, dim3(SUM_NT), s, o, p, peer_stride, y, nvec, t); break;
     OASES_SUM_CASE(0) OASES_SUM_CASE(1) OASES_SUM_CASE(2) OASES_SUM_CASE(3)
     OASES_SUM_CASE(4) OASES_SUM_CASE(5) OASES_SUM_CASE(6) OASES_SUM_CASE(7)
 #undef OASES_SUM_CASE
     default:
-      OASES_LAUNCH(allreduce_bf16_many_kernel, grid, dim3(SUM_NT), s, o, p, peer_stride, n_peers, y, nvec);
+      OASES_LAUNCH(allreduce_bf16_many_kernel, grid, dim3(SUM_NT), s, o, p, peer_stride, n_peers, y, nvec, t);
   }
   return hipSuccess;
 }
@@ -210,6 +386,45 @@ int allreduce_fused_wgs(int64_t nvec) {
   const int64_t cap = g_sum_grid_cap < 16 ? 8 : g_sum_grid_cap / 2;
   const int64_t w = want < cap ? want : cap;
   return (int)((w + 7) / 8 * 8);
+}
+
+hipError_t layer_norm_fwd(const void *x, const void *w, const void *b, void *z, int rows, int h, float eps,
+                          hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  OASES_LAUNCH(ln_fwd_kernel, dim3((rows + LN_ROWS - 1) / LN_ROWS), dim3(64 * LN_ROWS), s,
+               static_cast<const uint4 *>(x), static_cast<const uint4 *>(w), static_cast<const uint4 *>(b),
+               static_cast<uint4 *>(z), rows, h / 8, eps);
+  return hipGetLastError();
+}
+
+int64_t layer_norm_partial_floats(int rows, int h) {
+  return 2 * (int64_t)((rows + CS_ROWS - 1) / CS_ROWS) * h;
+}
+
+hipError_t layer_norm_bwd(const void *dz, const void *x, const void *w, const void *g, void *dx, float *stats,
+                          float *partial, float *dw, float *db, int rows, int h, float eps, int beta,
+                          hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  OASES_LAUNCH(ln_bwd_kernel, dim3((rows + LN_ROWS - 1) / LN_ROWS), dim3(64 * LN_ROWS), s,
+               static_cast<const uint4 *>(dz), static_cast<const uint4 *>(x), static_cast<const uint4 *>(w),
+               static_cast<const uint4 *>(g), static_cast<uint4 *>(dx), reinterpret_cast<float2 *>(stats), rows,
+               h / 8, eps);
+  const int nchunks = (rows + CS_ROWS - 1) / CS_ROWS;
+  float *pw = partial, *pb = partial + (int64_t)nchunks * h;
+  OASES_LAUNCH(ln_grad_pass1, dim3((h + 255) / 256, nchunks), dim3(256), s, static_cast<const bf16_t *>(dz),
+               static_cast<const bf16_t *>(x), reinterpret_cast<const float2 *>(stats), rows, h, pw, pb);
+  OASES_LAUNCH(colsum_pass2, dim3((h + 31) / 32), dim3(256), s, pw, nchunks, h, dw, beta);
+  OASES_LAUNCH(colsum_pass2, dim3((h + 31) / 32), dim3(256), s, pb, nchunks, h, db, beta);
+  return hipGetLastError();
+}
+
+hipError_t dropout_bwd(const void *g, void *out, int64_t n, const DropRes &t, hipStream_t s) {
+  const int64_t nvec = n / 8;
+  if (nvec <= 0) return hipSuccess;
+  const int64_t want = (nvec + SUM_NT - 1) / SUM_NT;
+  OASES_LAUNCH(dropout_bwd_kernel, dim3((unsigned)(want < 1024 ? want : 1024)), dim3(SUM_NT), s,
+               static_cast<const uint4 *>(g), static_cast<uint4 *>(out), nvec, t);
+  return hipGetLastError();
 }
 
 int64_t colsum_partial_floats(int rows, int cols) {

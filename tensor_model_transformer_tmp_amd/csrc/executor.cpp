@@ -51,6 +51,10 @@ size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Dims {
   int L, B, s, h, ns, d, fs, w, dtype, causal;
+  bool full;          // LayerNorm / dropout / residual around every block
+  int drop_q, tanh;   // dropout probability in 1/65536; tanh-form GeLU
+  uint64_t drop_seed;
+  float eps;
   int T, a, nb;  // tokens per sub-batch, attention width, sequences per sub-batch
   size_t esz;
   bool any_attn, any_ffn;
@@ -69,6 +73,9 @@ struct WsLayout {
   // offsets inside a slot
   size_t s_U, s_H, s_QKV, s_O, s_LSE;
   size_t colsum;
+  size_t s_Z;                     // full blocks: LayerNorm output in a slot
+  size_t dS[2], dZ[2], lnst[2];   // full blocks: dropout backward, C(B) sum, row statistics
+  size_t lnpart;                  // full blocks: LayerNorm weight-gradient partials
   size_t gbuf[2];
   size_t cr_out;
   size_t total;
@@ -86,14 +93,19 @@ WsLayout make_layout(const Dims &D, int mode) {
     o.dpre[sb] = take((size_t)D.T * D.max_n_in() * D.esz);
     o.dO[sb] = D.any_attn ? take((size_t)D.T * D.a * D.esz) : 0;
     o.delta[sb] = D.any_attn ? take(lse_bytes) : 0;
+    o.dS[sb] = D.full ? take(th) : 0;
+    o.dZ[sb] = D.full ? take(th) : 0;
+    o.lnst[sb] = D.full ? take((size_t)D.T * 2 * sizeof(float)) : 0;
   }
+  o.lnpart = D.full ? take((size_t)layer_norm_partial_floats(D.T, D.h) * sizeof(float)) : 0;
   // activation slot: FFN {U, H} or attention {QKV, O, LSE}; slot size is the max
   size_t ffn_sz = 0, attn_sz = 0;
   if (D.any_ffn) ffn_sz = 2 * align_up((size_t)D.T * D.fs * D.esz);
   if (D.any_attn)
     attn_sz = align_up((size_t)D.T * 3 * D.a * D.esz) + align_up((size_t)D.T * D.a * D.esz) +
               align_up(lse_bytes);
-  o.act_bytes = align_up(std::max(ffn_sz, attn_sz));
+  o.act_bytes = align_up(std::max(ffn_sz, attn_sz)) + (D.full ? align_up(th) : 0);
+  o.s_Z = align_up(std::max(ffn_sz, attn_sz));
   o.s_U = 0;
   o.s_H = D.any_ffn ? align_up((size_t)D.T * D.fs * D.esz) : 0;
   o.s_QKV = 0;
@@ -148,6 +160,18 @@ int check_config(const oases_config *cfg, Dims *D, std::string *err) {
   d.w = cfg->tmp_width; d.dtype = cfg->dtype; d.causal = cfg->causal;
   d.T = (int)T; d.a = d.ns * d.d; d.nb = d.B / 2;
   d.esz = cfg->dtype == OASES_BF16 ? 2 : 4;
+  if (cfg->full_block != 0 && cfg->full_block != 1) return fail(OASES_E_ARG, "full_block must be 0 or 1");
+  if (cfg->gelu_tanh != 0 && cfg->gelu_tanh != 1) return fail(OASES_E_ARG, "gelu_tanh must be 0 or 1");
+  if ((cfg->full_block || cfg->gelu_tanh) && cfg->dtype != OASES_BF16)
+    return fail(OASES_E_UNSUPPORTED, "full blocks and tanh GeLU need bf16 storage");
+  if (cfg->full_block && (cfg->drop_q < 0 || cfg->drop_q > 65535))
+    return fail(OASES_E_ARG, "drop_q must be in [0, 65535]");
+  if (cfg->full_block && !(cfg->ln_eps > 0.f)) return fail(OASES_E_ARG, "ln_eps must be > 0");
+  d.full = cfg->full_block == 1;
+  d.drop_q = d.full ? cfg->drop_q : 0;
+  d.drop_seed = cfg->drop_seed;
+  d.eps = cfg->ln_eps;
+  d.tanh = cfg->gelu_tanh;
   if (D) *D = std::move(d);
   return OASES_OK;
 }
@@ -253,6 +277,21 @@ struct Exec {
     const int i = W.n_slots == 1 ? 0 : l;
     return ws() + W.act0 + (size_t)(i * 2 + sb) * W.act_bytes;
   }
+  // the column GEMM's input: the block input, or (full blocks) its LayerNorm
+  const char *gemm_in(int l, int sb) const { return D().full ? slot(l, sb) + W.s_Z : layer_in(l, sb); }
+  // the full block's dropout + residual after block l's AllReduce point
+  DropRes tail(int l, int sb) const {
+    const Dims &d = D();
+    DropRes t{};
+    t.res = layer_in(l, sb);
+    t.seed = d.drop_seed;
+    t.layer = (uint64_t)l;
+    t.sb = (uint64_t)sb;
+    t.drop = d.drop_q > 0;
+    t.thr = t.drop ? (uint64_t)(65536 - d.drop_q) << 48 : 0;
+    t.scale = t.drop ? 65536.f / (float)(65536 - d.drop_q) : 1.f;
+    return t;
+  }
   const char *peers(const void *p, int l, int sb) const {
     const size_t per = (size_t)(D().w - 1) * th_bytes();
     return static_cast<const char *>(p) + (size_t)(l * 2 + sb) * per;
@@ -275,14 +314,17 @@ struct Exec {
   }
 
   int gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmArgs &g, hipStream_t s);
-  int sum(const void *own, const void *pr, void *out, hipStream_t s) {
-    if (fused) {  // deferred to the next GEMM launch (flush_pending at the latest)
+  // an AllReduce point, optionally with the full block's tail (t.res set);
+  // may_fuse: the sum may wait for the next GEMM launch (fused overlap)
+  int sum(const void *own, const void *pr, void *out, hipStream_t s, const DropRes &t = DropRes{},
+          bool may_fuse = true) {
+    if (fused && may_fuse) {  // deferred to the next GEMM launch (flush_pending at the latest)
       const int64_t n = (int64_t)D().T * D().h;
-      pending = FusedSum{own, pr, n, out, n / 8, D().w - 1, allreduce_fused_wgs(n / 8)};
+      pending = FusedSum{own, pr, n, out, n / 8, D().w - 1, allreduce_fused_wgs(n / 8), t};
       return OASES_OK;
     }
     if (int r = prof_begin(KC_SUM, s)) return r;
-    HIPX(allreduce_point(bf16(), own, pr, (int64_t)D().T * D().h, D().w - 1, out, (int64_t)D().T * D().h, s));
+    HIPX(allreduce_point(bf16(), own, pr, (int64_t)D().T * D().h, D().w - 1, out, (int64_t)D().T * D().h, s, &t));
     return prof_end(KC_SUM, s);
   }
 
@@ -291,25 +333,27 @@ struct Exec {
     if (!pending.wgs) return OASES_OK;
     const FusedSum f = pending;
     pending = FusedSum{};
-    fused = false;
-    const int r = sum(f.own, f.peers, f.out, c->cs);
-    fused = true;
-    return r;
+    return sum(f.own, f.peers, f.out, c->cs, f.tail, false);
   }
+
+  // gradient w.r.t. the partial sums of block l's AllReduce point (Eq. (1)):
+  // dY itself, or (full blocks) its dropout backward
+  const void *dP(int l, int sb) const { return D().full ? static_cast<const void *>(ws() + W.dS[sb]) : grad_out(l, sb); }
 
   // column part of block l (F or R): writes the slot's activations.
   int column_part(int l, int sb, bool keep_pre) {
     const Dims &d = D();
     const oases_layer_params &p = c->prm[l];
     char *sl = slot(l, sb);
-    const void *x = layer_in(l, sb);
+    if (d.full) HIPX(layer_norm_fwd(layer_in(l, sb), p.ln_w, p.ln_b, sl + W.s_Z, d.T, d.h, d.eps, c->cs));
+    const void *x = gemm_in(l, sb);
     if (d.blocks[l] == OASES_FFN) {
       GemmArgs g{};
       g.M = d.T; g.N = d.fs; g.K = d.h;
       g.A = x; g.lda = d.h; g.B = p.w_in; g.ldb = d.h;
       g.C = sl + W.s_H; g.ldc = d.fs; g.bias = p.b_in;
       g.pre = keep_pre ? sl + W.s_U : nullptr; g.ld_pre = d.fs;
-      return gemm(KC_GEMM_FWD, KC, KC, EPI_BIAS_GELU, g, c->cs);
+      return gemm(KC_GEMM_FWD, KC, KC, d.tanh ? EPI_BIAS_GELU_TANH : EPI_BIAS_GELU, g, c->cs);
     }
     GemmArgs g{};
     g.M = d.T; g.N = 3 * d.a; g.K = d.h;
@@ -347,7 +391,7 @@ struct Exec {
     hipStream_t s = overlap ? c->ss : c->cs;
     if (overlap) HIPX(hipStreamWaitEvent(s, c->evF[l * 2 + sb], 0));
     if (int r = sum(ws() + W.P[sb], D().w > 1 ? peers(c->buf.peers_fwd, l, sb) : nullptr,
-                    layer_out(l, sb), s))
+                    layer_out(l, sb), s, D().full ? tail(l, sb) : DropRes{}))
       return r;
     if (overlap) HIPX(hipEventRecord(c->evCF[l * 2 + sb], s));
     return OASES_OK;
@@ -358,21 +402,24 @@ struct Exec {
     return OASES_OK;
   }
   int op_CR(int l, int sb) {
-    return sum(ws() + W.P[sb], D().w > 1 ? peers(c->buf.peers_fwd, l, sb) : nullptr, ws() + W.cr_out, c->cs);
+    return sum(ws() + W.P[sb], D().w > 1 ? peers(c->buf.peers_fwd, l, sb) : nullptr, ws() + W.cr_out, c->cs,
+               D().full ? tail(l, sb) : DropRes{});
   }
   int op_BdX(int l, int sb) {
     const Dims &d = D();
     const oases_layer_params &p = c->prm[l];
     if (overlap && l < d.L - 1) HIPX(hipStreamWaitEvent(c->cs, c->evCB[(l + 1) * 2 + sb], 0));
     char *sl = slot(l, sb);
-    const void *dy = grad_out(l, sb);
+    const void *dy = dP(l, sb);
+    if (d.full)  // the AllReduce inputs' gradient: dropout backward of dY (Eq. (1))
+      HIPX(dropout_bwd(grad_out(l, sb), ws() + W.dS[sb], (int64_t)d.T * d.h, tail(l, sb), c->cs));
     char *dpre = ws() + W.dpre[sb];
     if (d.blocks[l] == OASES_FFN) {
       GemmArgs g{};  // dU = (dY W_out) * gelu'(U)
       g.M = d.T; g.N = d.fs; g.K = d.h;
       g.A = dy; g.lda = d.h; g.B = p.w_out; g.ldb = d.fs;
       g.C = dpre; g.ldc = d.fs; g.aux = sl + W.s_U; g.ld_aux = d.fs;
-      if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_GELU_BWD, g, c->cs)) return r;
+      if (int r = gemm(KC_GEMM_DX, KC, MC, d.tanh ? EPI_GELU_BWD_TANH : EPI_GELU_BWD, g, c->cs)) return r;
     } else {
       GemmArgs g{};  // dO = dY W_o
       g.M = d.T; g.N = d.a; g.K = d.h;
@@ -394,11 +441,22 @@ struct Exec {
     return OASES_OK;
   }
   int op_CB(int l, int sb) {
+    const Dims &d = D();
     hipStream_t s = overlap ? c->ss : c->cs;
     if (overlap) HIPX(hipStreamWaitEvent(s, c->evBdX[l * 2 + sb], 0));
-    if (int r = sum(ws() + W.dxo[sb], D().w > 1 ? peers(c->buf.peers_bwd, l, sb) : nullptr,
-                    grad_in(l, sb), s))
-      return r;
+    if (!d.full) {
+      if (int r = sum(ws() + W.dxo[sb], d.w > 1 ? peers(c->buf.peers_bwd, l, sb) : nullptr, grad_in(l, sb), s))
+        return r;
+    } else {  // the sum (never deferred: its LayerNorm backward follows at once), then
+      // dX = dY + LayerNorm backward of the sum, and the LayerNorm weight gradients
+      if (int r = sum(ws() + W.dxo[sb], d.w > 1 ? peers(c->buf.peers_bwd, l, sb) : nullptr, ws() + W.dZ[sb], s,
+                      DropRes{}, false))
+        return r;
+      const oases_layer_params &p = c->prm[l];
+      HIPX(layer_norm_bwd(ws() + W.dZ[sb], layer_in(l, sb), p.ln_w, grad_out(l, sb), grad_in(l, sb),
+                          reinterpret_cast<float *>(ws() + W.lnst[sb]), reinterpret_cast<float *>(ws() + W.lnpart),
+                          static_cast<float *>(p.dln_w), static_cast<float *>(p.dln_b), d.T, d.h, d.eps, sb, s));
+    }
     if (overlap) HIPX(hipEventRecord(c->evCB[l * 2 + sb], s));
     return OASES_OK;
   }
@@ -406,7 +464,7 @@ struct Exec {
     const Dims &d = D();
     const oases_layer_params &p = c->prm[l];
     char *sl = slot(l, sb);
-    const void *dy = grad_out(l, sb);
+    const void *dy = dP(l, sb);
     const char *dpre = ws() + W.dpre[sb];
     const int nmid = d.n_mid(l), nin = d.n_in(l);
     GemmArgs g{};  // dW_out[h, nmid] (+)= dY^T act
@@ -417,7 +475,7 @@ struct Exec {
     if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g, c->cs)) return r;
     GemmArgs g2{};  // dW_in[nin, h] (+)= dpre^T X
     g2.M = nin; g2.N = d.h; g2.K = d.T;
-    g2.A = dpre; g2.lda = nin; g2.B = layer_in(l, sb); g2.ldb = d.h;
+    g2.A = dpre; g2.lda = nin; g2.B = gemm_in(l, sb); g2.ldb = d.h;
     g2.C = p.dw_in; g2.ldc = d.h; g2.beta = sb;
     if (bf16()) {  // db_in (+)= column sums of dpre, computed by the same GEMM
       g2.colsum = static_cast<float *>(p.db_in);
@@ -545,9 +603,9 @@ int oases_bind(oases_ctx *c, const oases_buffers *b, const oases_layer_params *p
                                        std::to_string(need));
   for (int l = 0; l < D.L; ++l) {
     const oases_layer_params &q = per_layer[l];
-    const void *lp[] = {q.w_in, q.b_in, q.w_out, q.dw_in, q.db_in, q.dw_out};
-    const char *nm[] = {"w_in", "b_in", "w_out", "dw_in", "db_in", "dw_out"};
-    for (int i = 0; i < 6; ++i) {
+    const void *lp[] = {q.w_in, q.b_in, q.w_out, q.dw_in, q.db_in, q.dw_out, q.ln_w, q.ln_b, q.dln_w, q.dln_b};
+    const char *nm[] = {"w_in", "b_in", "w_out", "dw_in", "db_in", "dw_out", "ln_w", "ln_b", "dln_w", "dln_b"};
+    for (int i = 0; i < (D.full ? 10 : 6); ++i) {
       if (!lp[i]) return set_err(c, OASES_E_ARG, "layer " + std::to_string(l) + " " + nm[i] + " is NULL");
       if (!aligned16(lp[i]))
         return set_err(c, OASES_E_ALIGN, "layer " + std::to_string(l) + " " + nm[i] + " is not 16-byte aligned");
@@ -733,14 +791,16 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
   if ((a_layout != 0 && a_layout != 1) || (b_layout != 0 && b_layout != 1)) return OASES_E_ARG;
   const bool fwd = a_layout == 0 && b_layout == 0, dx = a_layout == 0 && b_layout == 1,
              dw = a_layout == 1 && b_layout == 1;
-  if (!((fwd && epilogue >= 0 && epilogue <= 2) || (dx && (epilogue == 0 || epilogue == 3)) ||
+  const bool tanh_epi = (epilogue == 6 || epilogue == 7) && dtype == OASES_BF16;
+  if (!((fwd && ((epilogue >= 0 && epilogue <= 2) || (epilogue == 6 && tanh_epi))) ||
+        (dx && (epilogue == 0 || epilogue == 3 || (epilogue == 7 && tanh_epi))) ||
         (dw && (epilogue == 4 || (epilogue == 5 && dtype == OASES_BF16)))))
     return OASES_E_UNSUPPORTED;
   if (m < 0 || n < 0 || k < 0 || n % 8) return OASES_E_ARG;
   if (m == 0 || n == 0) return OASES_OK;
   if (!a || !b || !c_) return OASES_E_ARG;
-  if ((epilogue == 1 || epilogue == 2) && !bias) return OASES_E_ARG;
-  if (epilogue == 3 && (!aux || ld_aux < n || ld_aux % 8)) return OASES_E_ARG;
+  if ((epilogue == 1 || epilogue == 2 || epilogue == 6) && !bias) return OASES_E_ARG;
+  if ((epilogue == 3 || epilogue == 7) && (!aux || ld_aux < n || ld_aux % 8)) return OASES_E_ARG;
   if (epilogue == 5 && (!pre || ((uintptr_t)pre & 3))) return OASES_E_ARG;
   // contiguous dimension of each operand: A: k (layout 0) or m (1); B: k (0) or n (1)
   const int a_cont = a_layout == 0 ? k : m, a_rows = a_layout == 0 ? m : k;

@@ -167,7 +167,10 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const
 template <int EPI, int TN>
 __device__ __forceinline__ void epilogue_row(const GemmArgs &g, int m, const int (&ncol)[TN][4],
                                              float (&v)[TN][4][4]) {
-  constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_GELU;
+  constexpr bool GELU = EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_TANH;
+  constexpr bool GELU_BWD = EPI == EPI_GELU_BWD || EPI == EPI_GELU_BWD_TANH;
+  constexpr bool TANH = EPI == EPI_BIAS_GELU_TANH || EPI == EPI_GELU_BWD_TANH;
+  constexpr bool BIAS = EPI == EPI_BIAS || GELU;
   uint2 in[TN][4];  // bias or aux (bf16 x 4)
   float4 old[TN][4];
 #pragma unroll
@@ -177,7 +180,7 @@ __device__ __forceinline__ void epilogue_row(const GemmArgs &g, int m, const int
       const int n = ncol[j][jj];
       if (n >= g.N) continue;
       if constexpr (BIAS) in[j][jj] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(g.bias) + n);
-      if constexpr (EPI == EPI_GELU_BWD)
+      if constexpr (GELU_BWD)
         in[j][jj] = *reinterpret_cast<const uint2 *>(static_cast<const bf16_t *>(g.aux) + (int64_t)m * g.ld_aux + n);
       if constexpr (EPI == EPI_F32)
         if (g.beta) old[j][jj] = *reinterpret_cast<const float4 *>(static_cast<float *>(g.C) + (int64_t)m * g.ldc + n);
@@ -199,16 +202,17 @@ __device__ __forceinline__ void epilogue_row(const GemmArgs &g, int m, const int
         x[0] += lo_f32(in[j][jj].x); x[1] += hi_f32(in[j][jj].x);
         x[2] += lo_f32(in[j][jj].y); x[3] += hi_f32(in[j][jj].y);
       }
-      if constexpr (EPI == EPI_BIAS_GELU) {
+      if constexpr (GELU) {
         if (g.pre)
           *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(g.pre) + (int64_t)m * g.ld_pre + n) =
               make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) x[ii] = gelu_f(x[ii]);
+        for (int ii = 0; ii < 4; ++ii) x[ii] = TANH ? gelu_tanh_f(x[ii]) : gelu_f(x[ii]);
       }
-      if constexpr (EPI == EPI_GELU_BWD) {
-        x[0] *= gelu_grad_f(lo_f32(in[j][jj].x)); x[1] *= gelu_grad_f(hi_f32(in[j][jj].x));
-        x[2] *= gelu_grad_f(lo_f32(in[j][jj].y)); x[3] *= gelu_grad_f(hi_f32(in[j][jj].y));
+      if constexpr (GELU_BWD) {
+        const float u[4] = {lo_f32(in[j][jj].x), hi_f32(in[j][jj].x), lo_f32(in[j][jj].y), hi_f32(in[j][jj].y)};
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) x[ii] *= TANH ? gelu_tanh_grad_f(u[ii]) : gelu_grad_f(u[ii]);
       }
       *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(g.C) + (int64_t)m * g.ldc + n) =
           make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
@@ -281,6 +285,9 @@ __device__ __forceinline__ void fused_sum(const FusedSum &f, int wg) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t v = v0 + u * stride;
+      if (v < f.nvec && f.tail.res)
+        drop_res8(acc[u], reinterpret_cast<const uint4 *>(f.tail.res)[v], v, f.tail.seed, f.tail.layer,
+                  f.tail.sb, f.tail.thr, f.tail.scale, f.tail.drop);
       if (v < f.nvec)
         out[v] = make_uint4(cvt_pk_bf16(acc[u][0], acc[u][1]), cvt_pk_bf16(acc[u][2], acc[u][3]),
                             cvt_pk_bf16(acc[u][4], acc[u][5]), cvt_pk_bf16(acc[u][6], acc[u][7]));
@@ -559,12 +566,14 @@ hipError_t gemm_bf16(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream
       case EPI_STORE: return dispatch_tile<KC, KC, EPI_STORE>(g, s);
       case EPI_BIAS: return dispatch_tile<KC, KC, EPI_BIAS>(g, s);
       case EPI_BIAS_GELU: return dispatch_tile<KC, KC, EPI_BIAS_GELU>(g, s);
+      case EPI_BIAS_GELU_TANH: return dispatch_tile<KC, KC, EPI_BIAS_GELU_TANH>(g, s);
       default: break;
     }
   } else if (la == KC && lb == MC) {
     switch (epi) {
       case EPI_STORE: return dispatch_tile<KC, MC, EPI_STORE>(g, s);
       case EPI_GELU_BWD: return dispatch_tile<KC, MC, EPI_GELU_BWD>(g, s);
+      case EPI_GELU_BWD_TANH: return dispatch_tile<KC, MC, EPI_GELU_BWD_TANH>(g, s);
       default: break;
     }
   } else if (la == MC && lb == MC) {

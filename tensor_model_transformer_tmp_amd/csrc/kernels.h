@@ -46,7 +46,9 @@ enum Epi : int {
   EPI_BIAS = 1,       // C = acc + bias[n]
   EPI_BIAS_GELU = 2,  // pre = acc + bias[n] (optional), C = gelu(acc + bias[n])
   EPI_GELU_BWD = 3,   // C = acc * gelu'(aux[m][n])
-  EPI_F32 = 4         // C(float32) = acc (+ C if beta)
+  EPI_F32 = 4,        // C(float32) = acc (+ C if beta)
+  EPI_BIAS_GELU_TANH = 6,  // EPI_BIAS_GELU with the tanh form of GeLU (bf16)
+  EPI_GELU_BWD_TANH = 7    // EPI_GELU_BWD with the tanh form of GeLU (bf16)
 };
 
 // Operand layouts: for A(m,k): KC = stored [M][lda] (k contiguous),
@@ -57,6 +59,19 @@ enum Layout : int { KC = 0, MC = 1 };
 // An AllReduce-point sum (out = own + peers[0..np), float32 adds in that
 // order, one rounding) that a GEMM launch runs on extra workgroups beside its
 // tiles (sum_wgs of them; none when 0).  Same arithmetic as allreduce_point.
+// Replicated tail of a full transformer block applied to an AllReduce
+// point's sum S (bf16): out = res + dropout(S), elementwise.  Element e of the
+// [T_sb, h] sub-batch buffer is kept iff output word e % 4 of
+// Philox4x64-10 at counter (e / 4, sb, 0, 0) under key (seed, layer) is
+// below thr; kept elements are scaled by `scale` = 1 / (1 - p).  res null:
+// no tail (out = S).  drop 0: no dropout (out = res + S).
+struct DropRes {
+  const void *res;
+  uint64_t seed, layer, sb, thr;
+  float scale;
+  int drop;
+};
+
 struct FusedSum {
   const void *own;
   const void *peers;
@@ -65,6 +80,7 @@ struct FusedSum {
   int64_t nvec;         // 8-element vectors (n / 8)
   int np;
   int wgs;
+  DropRes tail;  // res null: none
 };
 
 struct GemmArgs {
@@ -94,9 +110,26 @@ hipError_t gemm_bf16(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream
 hipError_t gemm_f32(Layout la, Layout lb, Epi epi, const GemmArgs &g, hipStream_t s);
 void gemm_bf16_set_variant(int v);
 
-// AllReduce point: out = own + sum_k peers[k] (float32 accumulation in order)
+// AllReduce point: out = own + sum_k peers[k] (float32 accumulation in order),
+// followed by the full block's dropout + residual tail when `tail` has a
+// residual (bf16 only)
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
-                           int n_peers, void *out, int64_t n, hipStream_t s);
+                           int n_peers, void *out, int64_t n, hipStream_t s,
+                           const DropRes *tail = nullptr);
+
+// ---- full transformer block (bf16) ----
+// z = LayerNorm(x) * w + b per row of x [rows, h] (biased variance, eps)
+hipError_t layer_norm_fwd(const void *x, const void *w, const void *b, void *z, int rows, int h, float eps,
+                          hipStream_t s);
+// dx = g + LayerNorm backward of dz at x (weight w); dw (+)= sum_rows dz * xhat,
+// db (+)= sum_rows dz (beta: accumulate).  stats: 2*rows floats; partial:
+// layer_norm_partial_floats(rows, h) floats.
+hipError_t layer_norm_bwd(const void *dz, const void *x, const void *w, const void *g, void *dx,
+                          float *stats, float *partial, float *dw, float *db, int rows, int h, float eps,
+                          int beta, hipStream_t s);
+int64_t layer_norm_partial_floats(int rows, int h);
+// out = dropout backward of g (the mask and scale of `t`), n elements
+hipError_t dropout_bwd(const void *g, void *out, int64_t n, const DropRes &t, hipStream_t s);
 // largest grid (workgroups) of the AllReduce-point kernel
 void allreduce_set_grid_cap(int cap);
 // workgroups that run an AllReduce point of nvec 8-element vectors fused into

@@ -51,6 +51,11 @@ class DeviceShard:
                 "dw_in": torch.zeros(cfg.n_in(l), h, dtype=torch.float32, device=self.device),
                 "db_in": torch.zeros(cfg.n_in(l), dtype=torch.float32, device=self.device),
                 "dw_out": torch.zeros(h, cfg.n_mid(l), dtype=torch.float32, device=self.device)})
+            if getattr(cfg, "full_block", False):
+                self.params[-1].update({
+                    "ln_w": up(inp.ln_w[l]), "ln_b": up(inp.ln_b[l]),
+                    "dln_w": torch.zeros(h, dtype=torch.float32, device=self.device),
+                    "dln_b": torch.zeros(h, dtype=torch.float32, device=self.device)})
         self.ctx = shard.ShardContext(cfg)
         self.ctx.bind({"x": self.x, "y": self.y, "dy": self.dy, "dx": self.dx, "ckpt": self.ckpt,
                        "peers_fwd": self.peers_fwd, "peers_bwd": self.peers_bwd,
@@ -69,8 +74,9 @@ class DeviceShard:
         """Storage-form host copies of Y, dX and the float32 gradients."""
         torch.cuda.synchronize(self.device)
         out = {"Y": to_storage(self.y), "dX": to_storage(self.dx), "grads": []}
+        names = ("dw_in", "db_in", "dw_out") + (("dln_w", "dln_b") if getattr(self.cfg, "full_block", False) else ())
         for p in self.params:
-            out["grads"].append({k: p[k].cpu().numpy() for k in ("dw_in", "db_in", "dw_out")})
+            out["grads"].append({k: p[k].cpu().numpy() for k in names})
         return out
 
     def close(self):

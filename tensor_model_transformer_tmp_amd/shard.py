@@ -44,11 +44,14 @@ class Config(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("heads_per_shard", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn_shard", ctypes.c_int32),
                 ("tmp_width", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("causal", ctypes.c_int32)]
+                ("causal", ctypes.c_int32), ("full_block", ctypes.c_int32),
+                ("drop_q", ctypes.c_int32), ("drop_seed", ctypes.c_uint64),
+                ("ln_eps", ctypes.c_float), ("gelu_tanh", ctypes.c_int32)]
 
 
 class LayerParams(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w_in", "b_in", "w_out", "dw_in", "db_in", "dw_out")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_in", "b_in", "w_out", "dw_in", "db_in", "dw_out",
+                                                 "ln_w", "ln_b", "dln_w", "dln_b")]
 
 
 class Buffers(ctypes.Structure):
@@ -117,9 +120,12 @@ def _stream_handle(stream):
 def make_config(cfg) -> tuple:
     """ctypes Config from a ShardConfig-like object (keeps the blocks array alive)."""
     blocks = (ctypes.c_int32 * cfg.n_layers)(*cfg.blocks)
+    full = bool(getattr(cfg, "full_block", False))
     c = Config(cfg.n_layers, ctypes.cast(blocks, ctypes.POINTER(ctypes.c_int32)), cfg.micro_batch,
                cfg.seq, cfg.hidden, cfg.heads_per_shard, cfg.head_dim, cfg.ffn_shard,
-               cfg.tmp_width, cfg.dtype, int(cfg.causal))
+               cfg.tmp_width, cfg.dtype, int(cfg.causal), int(full),
+               int(getattr(cfg, "drop_q", 0)) if full else 0, int(getattr(cfg, "drop_seed", 0)),
+               float(getattr(cfg, "ln_eps", 1e-5)), int(bool(getattr(cfg, "gelu_tanh", False))))
     return c, blocks
 
 
@@ -151,15 +157,16 @@ class ShardContext:
 
     def bind(self, bufs: dict, params: list):
         """bufs: x, y, dy, dx, ckpt, peers_fwd, peers_bwd, workspace (torch tensors or None).
-        params: per layer dict w_in, b_in, w_out, dw_in, db_in, dw_out."""
+        params: per layer dict w_in, b_in, w_out, dw_in, db_in, dw_out (and ln_w, ln_b,
+        dln_w, dln_b for full blocks)."""
         ws = bufs["workspace"]
         b = Buffers(*[_ptr(bufs.get(n)) for n in ("x", "y", "dy", "dx", "ckpt", "peers_fwd",
                                                   "peers_bwd", "workspace")],
                     ws.numel() * ws.element_size())
         arr = (LayerParams * self.cfg.n_layers)()
         for l, p in enumerate(params):
-            arr[l] = LayerParams(*[_ptr(p[n]) for n in ("w_in", "b_in", "w_out", "dw_in", "db_in",
-                                                         "dw_out")])
+            arr[l] = LayerParams(*[_ptr(p.get(n)) for n in ("w_in", "b_in", "w_out", "dw_in", "db_in",
+                                                             "dw_out", "ln_w", "ln_b", "dln_w", "dln_b")])
         self._check(lib().oases_bind(self.h, ctypes.byref(b), arr), "oases_bind")
         self._keep = [bufs, params]
 
@@ -238,7 +245,8 @@ def allreduce_point(dtype, own, peers, n_peers, out, stream=None):
                 "oases_allreduce_point")
 
 
-EPILOGUES = {"store": 0, "bias": 1, "gelu": 2, "gelu_bwd": 3, "f32": 4, "f32_colsum": 5}
+EPILOGUES = {"store": 0, "bias": 1, "gelu": 2, "gelu_bwd": 3, "f32": 4, "f32_colsum": 5, "gelu_tanh": 6,
+             "gelu_tanh_bwd": 7}
 
 
 def gemm(dtype, a, b, c, a_layout=0, b_layout=0, epilogue="store", m=None, n=None, k=None,

@@ -46,6 +46,19 @@ def test_create_validation():
         assert ei.value.code == code, bad
     # fp32 FFN-only stacks are supported
     shard.ShardContext(gen.PRESETS["c1_ffn_fp32"]).close()
+    # full transformer blocks: bf16 only, drop_q in [0, 65535], eps > 0
+    full = dict(full_block=True, drop_q=6554)
+    for bad, code in ((dict(drop_q=65536), shard.E_ARG), (dict(drop_q=-1), shard.E_ARG),
+                      (dict(ln_eps=0.0), shard.E_ARG)):
+        with pytest.raises(shard.OasesError) as ei:
+            shard.ShardContext(_cfg(**{**full, **bad}))
+        assert ei.value.code == code, bad
+    for cfg in (gen.PRESETS["c1_ffn_fp32"].with_(full_block=True),
+                gen.PRESETS["c1_ffn_fp32"].with_(gelu_tanh=True)):
+        with pytest.raises(shard.OasesError) as ei:
+            shard.ShardContext(cfg)
+        assert ei.value.code == shard.E_UNSUPPORTED
+    shard.ShardContext(_cfg(**full, gelu_tanh=True)).close()
 
 
 def test_workspace_bytes_modes():

@@ -43,7 +43,7 @@ def test_allreduce_point_bit_exact(dtype, n, n_peers):
 
 @pytest.mark.parametrize("m,n,k", [(200, 192, 128), (1000, 520, 576), (2048, 1024, 1024),
                                    (4096, 3072, 512), (37, 8, 8)])
-@pytest.mark.parametrize("epi", ["store", "bias", "gelu"])
+@pytest.mark.parametrize("epi", ["store", "bias", "gelu", "gelu_tanh"])
 def test_gemm_fwd_bf16(m, n, k, epi):
     rng = np.random.default_rng(m * 7 + n + k)
     a, w = _bf16_bits(rng, (m, k)), _bf16_bits(rng, (n, k), 0.05)
@@ -51,15 +51,18 @@ def test_gemm_fwd_bf16(m, n, k, epi):
     dev = "cuda"
     ta, tw, tb = (to_device(x, gen.BF16, dev) for x in (a, w, b))
     c = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-    pre = torch.empty_like(c) if epi == "gelu" else None
-    shard.gemm_fwd(shard.BF16, ta, tw, c, bias=None if epi == "store" else tb,
-                   gelu=epi == "gelu", pre=pre)
+    pre = torch.empty_like(c) if epi.startswith("gelu") else None
+    if epi == "gelu_tanh":
+        shard.gemm(shard.BF16, ta, tw, c, 0, 0, "gelu_tanh", bias=tb, pre=pre)
+    else:
+        shard.gemm_fwd(shard.BF16, ta, tw, c, bias=None if epi == "store" else tb,
+                       gelu=epi == "gelu", pre=pre)
     torch.cuda.synchronize()
     af, wf, bf = (gen.bf16_bits_to_f64(x) for x in (a, w, b))
     ref = af @ wf.T + (0 if epi == "store" else bf)
-    if epi == "gelu":
+    if epi.startswith("gelu"):
         assert_close(gen.bf16_bits_to_f64(to_storage(pre)), ref, 8e-3, "pre-activation")
-        ref = blocks.gelu(ref)
+        ref = blocks.gelu_tanh(ref) if epi == "gelu_tanh" else blocks.gelu(ref)
     got = gen.bf16_bits_to_f64(to_storage(c))
     assert_close(got, ref, 8e-3, f"C {m}x{n}x{k} {epi}")
     np.testing.assert_allclose(got, ref, rtol=1.6e-2, atol=1e-2 * np.abs(ref).max())
@@ -114,7 +117,7 @@ GEMM_SHAPES = [(200, 192, 128), (1000, 520, 576), (2048, 1024, 1024), (296, 136,
 
 
 @pytest.mark.parametrize("variant", list(range(20)))
-@pytest.mark.parametrize("kind", ["fwd", "dx", "dx_gelu", "dw", "dw_colsum"])
+@pytest.mark.parametrize("kind", ["fwd", "dx", "dx_gelu", "dx_gelu_tanh", "dw", "dw_colsum"])
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 def test_gemm_layouts_and_tiles(variant, kind, m, n, k):
     """Every operand layout / epilogue of the step's GEMMs and every tile
@@ -136,12 +139,14 @@ def test_gemm_layouts_and_tiles(variant, kind, m, n, k):
             b_kn = np.ascontiguousarray(b_nk.T)  # stored [K][N] (n contiguous)
             c = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
             aux = None
-            if kind == "dx_gelu":
+            if kind.startswith("dx_gelu"):
                 u = _bf16_bits(rng, (m, n))
                 aux = to_device(u, gen.BF16, dev)
-                ref = ref * blocks.gelu_grad(gen.bf16_bits_to_f64(u))
+                grad = blocks.gelu_tanh_grad if kind == "dx_gelu_tanh" else blocks.gelu_grad
+                ref = ref * grad(gen.bf16_bits_to_f64(u))
+            epi = {"dx": "store", "dx_gelu": "gelu_bwd", "dx_gelu_tanh": "gelu_tanh_bwd"}[kind]
             shard.gemm(shard.BF16, to_device(a_km, gen.BF16, dev), to_device(b_kn, gen.BF16, dev), c,
-                       0, 1, "gelu_bwd" if aux is not None else "store", m=m, n=n, k=k, aux=aux)
+                       0, 1, epi, m=m, n=n, k=k, aux=aux)
         else:
             a_mk = np.ascontiguousarray(a_km.T)  # stored [K][M] (m contiguous)
             b_kn = np.ascontiguousarray(b_nk.T)

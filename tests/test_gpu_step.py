@@ -37,12 +37,23 @@ SMALL = {
 }
 
 
+# full transformer blocks (LayerNorm, dropout, residual; tanh GeLU in one of them)
+FULL = {
+    "full_pair_d64": SMALL["pair_d64_ragged"].with_(name="full_pair_d64", full_block=True, drop_q=6554,
+                                                  drop_seed=123),
+    "full_pair_d128_tanh": SMALL["pair_d128"].with_(name="full_pair_d128_tanh", full_block=True,
+                                                    drop_q=13107, gelu_tanh=True),
+    "full_stack4_nodrop": SMALL["stack4_d64"].with_(name="full_stack4_nodrop", full_block=True, drop_q=0),
+}
+
+
 def _compare(cfg, got, ref, tol):
     dec = lambda a: gen.storage_to_f64(a, cfg.dtype)
     assert_close(dec(got["Y"]), ref["Y"], tol, f"{cfg.name} Y")
     assert_close(dec(got["dX"]), ref["dX"], tol, f"{cfg.name} dX")
+    names = ("dw_in", "db_in", "dw_out") + (("dln_w", "dln_b") if cfg.full_block else ())
     for l in range(cfg.n_layers):
-        for n in ("dw_in", "db_in", "dw_out"):
+        for n in names:
             assert_close(got["grads"][l][n], ref["grads"][l][n], tol, f"{cfg.name} layer {l} {n}")
 
 
@@ -133,3 +144,32 @@ def test_attention_variants_full_step(variant, name):
     finally:
         shard.set_attention_variant(0)
     _compare(cfg, got, ref, 2e-2)
+
+
+@pytest.mark.parametrize("name", list(FULL))
+@pytest.mark.parametrize("zero_peers", [False, True])
+def test_full_block_step_matches_oracle(name, zero_peers):
+    """Full transformer blocks: every output and gradient (LayerNorm weights
+    included) against the oracle, and every schedule, hipGraph replay and the
+    per-layer entry points bit-identical to the overlapped step."""
+    cfg = FULL[name]
+    inp = gen.make_inputs(cfg, zero_peers=zero_peers)
+    ref = oschedule.run_step(inp, "serial_fine")
+    dev = DeviceShard(inp, modes=MODES)
+    dev.step("overlap_fine")
+    got = dev.results()
+    _compare(cfg, got, ref, 2e-2)
+    for mode in MODES:
+        for graph in (False, True):
+            dev.step(mode, use_graph=graph)
+            _bitwise_equal(dev.results(), got)
+    L = cfg.n_layers
+    for l in range(L):
+        for sb in (0, 1):
+            dev.ctx.layer_fwd(l, sb)
+    for l in reversed(range(L)):
+        for sb in (0, 1):
+            dev.ctx.layer_bwd_recompute(l, sb)
+    dev.ctx.sync()
+    _bitwise_equal(dev.results(), got)
+    dev.close()
