@@ -279,12 +279,16 @@ def study_density(names, reps=20):
     return {"study": "batch_split_density", "reps": reps, "blocks": res}
 
 
+def _preset(name):
+    return gen.PRESETS[name] if name in gen.PRESETS else gen.FULL_PRESETS[name]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default=DEFAULT_WORKLOAD, choices=gen.PRESET_ORDER)
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD, choices=gen.PRESET_ORDER + list(gen.FULL_PRESETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-kernel", default=None, choices=list(KERNEL_CLASSES),
                     help="kernel class for the roofline entry (default: most time per step)")
@@ -303,7 +307,7 @@ def main():
         sys.exit(2)
 
     if args.study == "ablation":
-        print(json.dumps(study_ablation(gen.PRESETS[args.config], args.steps, args.warmup)), flush=True)
+        print(json.dumps(study_ablation(_preset(args.config), args.steps, args.warmup)), flush=True)
         return 0
     if args.study == "density":
         names = [n for n in gen.PRESET_ORDER if gen.PRESETS[n].dtype == gen.BF16]
@@ -313,7 +317,7 @@ def main():
     import torch
     from tensor_model_transformer_tmp_amd.device import DeviceShard
 
-    cfg = gen.PRESETS[args.config]
+    cfg = _preset(args.config)
     inp = gen.make_inputs(cfg)
     dev = DeviceShard(inp, device="cuda:0", modes=("overlap_fine", "overlap_fused", "serial_fine"))
     del inp
@@ -400,7 +404,9 @@ def main():
                    "heads_per_shard": cfg.heads_per_shard, "head_dim": cfg.head_dim,
                    "ffn_shard": cfg.ffn_shard, "tmp_width": cfg.tmp_width,
                    "schedule": mode + "+" + ("hipGraph" if use_graph else "eager"),
-                   "parallelism": "one TMP shard, 1 GPU"},
+                   "parallelism": "one TMP shard, 1 GPU",
+                   **({"full_block": True, "dropout_p": cfg.drop_q / 65536.0, "gelu_tanh": cfg.gelu_tanh}
+                      if cfg.full_block else {})},
         "mfma_peak_frac": value / MFMA_BF16_PEAK_TFLOPS,
         "reduction_hidden_frac": hidden,
         "serial_ms_per_step": sec_serial * 1e3,

@@ -129,6 +129,13 @@ PRESETS = {
 }
 PRESET_ORDER = list(PRESETS)
 
+# The same shapes wrapped as full transformer blocks (LayerNorm before every
+# block, dropout p = 0.1 and the residual add after every AllReduce point).
+FULL_PRESETS = {
+    "c2_full_h1024": PRESETS["c2_pair_h1024"].with_(name="c2_full_h1024", full_block=True, drop_q=6554),
+    "c5_full_h8192": PRESETS["c5_pair_h8192"].with_(name="c5_full_h8192", full_block=True, drop_q=6554),
+}
+
 
 # ----------------------------------------------------------------------------
 # storage-type rounding of drawn values (input formatting only)
