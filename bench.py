@@ -164,7 +164,7 @@ def copy_calibration(nbytes):
 # ---------------------------------------------------------------------------
 
 ABLATION_MODES = ("serial_norecompute", "serial_default", "serial_fine", "overlap_fine",
-                  "overlap_fused")
+                  "overlap_fused", "overlap_streams")
 
 
 def study_ablation(cfg, steps, warmup):
@@ -319,7 +319,8 @@ def main():
 
     cfg = _preset(args.config)
     inp = gen.make_inputs(cfg)
-    dev = DeviceShard(inp, device="cuda:0", modes=("overlap_fine", "overlap_fused", "serial_fine"))
+    dev = DeviceShard(inp, device="cuda:0", modes=("overlap_fine", "overlap_fused", "overlap_streams",
+                                                    "serial_fine"))
     del inp
 
     def run(mode, graph, n):
@@ -334,15 +335,16 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
-    # The overlapped fine-grained schedule has two realisations: the sums on
-    # a side stream ordered with events (overlap_fine), or the sums as extra
+    # The overlapped fine-grained schedule has three realisations: the sums on
+    # a side stream ordered with events (overlap_fine), the sums as extra
     # workgroups of the next GEMM launch on the compute stream
-    # (overlap_fused).  Each is issued eagerly or replayed as one hipGraph;
-    # all four are probed briefly and the fastest is the timed region.  The
-    # same kernels serialised on one stream give the reference for the
-    # hidden-reduction estimate.
+    # (overlap_fused), or one stream per sub-batch carrying its compute and
+    # its sums (overlap_streams).  Each is issued eagerly or replayed as one
+    # hipGraph; all six are probed briefly and the fastest is the timed
+    # region.  The same kernels serialised on one stream give the reference
+    # for the hidden-reduction estimate.
     probe = max(3, args.steps // 5)
-    launch = {(m, g): timed(m, g, probe, 2) for m in ("overlap_fine", "overlap_fused")
+    launch = {(m, g): timed(m, g, probe, 2) for m in ("overlap_fine", "overlap_fused", "overlap_streams")
               for g in (False, True)}
     mode, use_graph = min(launch, key=launch.get)
     sec = timed(mode, use_graph, args.steps, args.warmup)

@@ -81,14 +81,20 @@ typedef enum { OASES_ATTN = 0, OASES_FFN = 1 } oases_block;
  * stream).  The SERIAL modes issue everything on the compute stream.
  * DEFAULT_RECOMPUTE recomputes the whole block including its row GEMM and
  * issues C(R) (its result is discarded); NO_RECOMPUTE keeps every block's
- * intermediates from the forward pass (needs a larger workspace).  All modes
- * give bit-identical results. */
+ * intermediates from the forward pass (needs a larger workspace).
+ * OVERLAP_STREAMS issues the same op list with one stream per sub-batch:
+ * sub-batch 0's compute and AllReduce points on the compute stream,
+ * sub-batch 1's on the side stream, so each sub-batch's sums and kernels run
+ * beside the other's; the only cross-stream edges order the two
+ * sub-batches' weight-gradient accumulation (and a fork and join per step).
+ * All modes give bit-identical results. */
 typedef enum {
   OASES_OVERLAP_FINE = 0,
   OASES_SERIAL_FINE = 1,
   OASES_SERIAL_DEFAULT_RECOMPUTE = 2,
   OASES_SERIAL_NO_RECOMPUTE = 3,
-  OASES_OVERLAP_FUSED = 4
+  OASES_OVERLAP_FUSED = 4,
+  OASES_OVERLAP_STREAMS = 5
 } oases_mode;
 
 /* Shape of the shard.  Constraints (OASES_E_SHAPE otherwise):

@@ -72,10 +72,10 @@ struct WsLayout {
   int n_slots;
   // offsets inside a slot
   size_t s_U, s_H, s_QKV, s_O, s_LSE;
-  size_t colsum;
+  size_t colsum[2];  // per sub-batch: the sub-batches' column sums may run concurrently
   size_t s_Z;                     // full blocks: LayerNorm output in a slot
   size_t dS[2], dZ[2], lnst[2];   // full blocks: dropout backward, C(B) sum, row statistics
-  size_t lnpart;                  // full blocks: LayerNorm weight-gradient partials
+  size_t lnpart[2];               // full blocks: LayerNorm weight-gradient partials
   size_t gbuf[2];
   size_t cr_out;
   size_t total;
@@ -97,7 +97,8 @@ WsLayout make_layout(const Dims &D, int mode) {
     o.dZ[sb] = D.full ? take(th) : 0;
     o.lnst[sb] = D.full ? take((size_t)D.T * 2 * sizeof(float)) : 0;
   }
-  o.lnpart = D.full ? take((size_t)layer_norm_partial_floats(D.T, D.h) * sizeof(float)) : 0;
+  for (int sb = 0; sb < 2; ++sb)
+    o.lnpart[sb] = D.full ? take((size_t)layer_norm_partial_floats(D.T, D.h) * sizeof(float)) : 0;
   // activation slot: FFN {U, H} or attention {QKV, O, LSE}; slot size is the max
   size_t ffn_sz = 0, attn_sz = 0;
   if (D.any_ffn) ffn_sz = 2 * align_up((size_t)D.T * D.fs * D.esz);
@@ -113,7 +114,7 @@ WsLayout make_layout(const Dims &D, int mode) {
   o.s_LSE = D.any_attn ? o.s_O + align_up((size_t)D.T * D.a * D.esz) : 0;
   o.n_slots = (mode == OASES_SERIAL_NO_RECOMPUTE) ? D.L : 1;
   o.act0 = take(o.act_bytes * 2 * o.n_slots);
-  o.colsum = take((size_t)colsum_partial_floats(D.T, D.max_n_in()) * sizeof(float));
+  for (int sb = 0; sb < 2; ++sb) o.colsum[sb] = take((size_t)colsum_partial_floats(D.T, D.max_n_in()) * sizeof(float));
   if (D.L > 1) {
     o.gbuf[0] = take((size_t)2 * th);
     o.gbuf[1] = take((size_t)2 * th);
@@ -179,18 +180,19 @@ int check_config(const oases_config *cfg, Dims *D, std::string *err) {
 std::vector<Op> build_ops(int L, int mode) {
   std::vector<Op> ops;
   const int side = (mode == OASES_OVERLAP_FINE || mode == OASES_OVERLAP_FUSED) ? 1 : 0;
+  const bool by_sb = mode == OASES_OVERLAP_STREAMS;  // stream = sub-batch
   for (int l = 0; l < L; ++l)
     for (int sb = 0; sb < 2; ++sb) {
-      ops.push_back({OP_F, l, sb, 0});
-      ops.push_back({OP_CF, l, sb, side});
+      ops.push_back({OP_F, l, sb, by_sb ? sb : 0});
+      ops.push_back({OP_CF, l, sb, by_sb ? sb : side});
     }
   for (int l = L - 1; l >= 0; --l)
     for (int sb = 0; sb < 2; ++sb) {
-      if (mode != OASES_SERIAL_NO_RECOMPUTE) ops.push_back({OP_R, l, sb, 0});
+      if (mode != OASES_SERIAL_NO_RECOMPUTE) ops.push_back({OP_R, l, sb, by_sb ? sb : 0});
       if (mode == OASES_SERIAL_DEFAULT_RECOMPUTE) ops.push_back({OP_CR, l, sb, 0});
-      ops.push_back({OP_BDX, l, sb, 0});
-      ops.push_back({OP_CB, l, sb, side});
-      ops.push_back({OP_BDW, l, sb, 0});
+      ops.push_back({OP_BDX, l, sb, by_sb ? sb : 0});
+      ops.push_back({OP_CB, l, sb, by_sb ? sb : side});
+      ops.push_back({OP_BDW, l, sb, by_sb ? sb : 0});
     }
   return ops;
 }
@@ -207,7 +209,8 @@ struct oases_ctx {
   hipStream_t cs = nullptr, ss = nullptr;
   bool streams_set = false;
   std::vector<hipEvent_t> evF, evCF, evBdX, evCB;
-  hipGraphExec_t gexec[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  std::vector<hipEvent_t> evSB;  // OVERLAP_STREAMS: B_dW(l, 0) done [l < L], fork [L], join [L+1]
+  hipGraphExec_t gexec[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   std::vector<uint8_t> fwd_done, bwd_done;
   std::string err;
   // timing instrumentation
@@ -243,6 +246,10 @@ struct Exec {
   const WsLayout &W;
   int mode;
   bool overlap;  // side stream distinct from the compute stream
+  // OVERLAP_STREAMS: every op of sub-batch 1 (compute and its AllReduce
+  // points) on the side stream, of sub-batch 0 on the compute stream
+  bool by_sb = false;
+  hipStream_t cst(int sb) const { return by_sb && sb == 1 ? c->ss : c->cs; }
   // OVERLAP_FUSED (bf16): an AllReduce point waits here and runs as extra
   // workgroups of the next GEMM launched on the compute stream
   bool fused = false;
@@ -345,7 +352,7 @@ struct Exec {
     const Dims &d = D();
     const oases_layer_params &p = c->prm[l];
     char *sl = slot(l, sb);
-    if (d.full) HIPX(layer_norm_fwd(layer_in(l, sb), p.ln_w, p.ln_b, sl + W.s_Z, d.T, d.h, d.eps, c->cs));
+    if (d.full) HIPX(layer_norm_fwd(layer_in(l, sb), p.ln_w, p.ln_b, sl + W.s_Z, d.T, d.h, d.eps, cst(sb)));
     const void *x = gemm_in(l, sb);
     if (d.blocks[l] == OASES_FFN) {
       GemmArgs g{};
@@ -353,17 +360,17 @@ struct Exec {
       g.A = x; g.lda = d.h; g.B = p.w_in; g.ldb = d.h;
       g.C = sl + W.s_H; g.ldc = d.fs; g.bias = p.b_in;
       g.pre = keep_pre ? sl + W.s_U : nullptr; g.ld_pre = d.fs;
-      return gemm(KC_GEMM_FWD, KC, KC, d.tanh ? EPI_BIAS_GELU_TANH : EPI_BIAS_GELU, g, c->cs);
+      return gemm(KC_GEMM_FWD, KC, KC, d.tanh ? EPI_BIAS_GELU_TANH : EPI_BIAS_GELU, g, cst(sb));
     }
     GemmArgs g{};
     g.M = d.T; g.N = 3 * d.a; g.K = d.h;
     g.A = x; g.lda = d.h; g.B = p.w_in; g.ldb = d.h;
     g.C = sl + W.s_QKV; g.ldc = 3 * d.a; g.bias = p.b_in;
-    if (int r = gemm(KC_GEMM_FWD, KC, KC, EPI_BIAS, g, c->cs)) return r;
-    if (int r = prof_begin(KC_ATTN_FWD, c->cs)) return r;
+    if (int r = gemm(KC_GEMM_FWD, KC, KC, EPI_BIAS, g, cst(sb))) return r;
+    if (int r = prof_begin(KC_ATTN_FWD, cst(sb))) return r;
     HIPX(attention_fwd(d.nb, d.s, d.ns, d.d, d.causal, sl + W.s_QKV, sl + W.s_O,
-                       reinterpret_cast<float *>(sl + W.s_LSE), c->cs));
-    return prof_end(KC_ATTN_FWD, c->cs);
+                       reinterpret_cast<float *>(sl + W.s_LSE), cst(sb)));
+    return prof_end(KC_ATTN_FWD, cst(sb));
   }
 
   // row-parallel GEMM of block l: partial P[sb] = act W_out^T
@@ -376,19 +383,19 @@ struct Exec {
     g.A = d.blocks[l] == OASES_FFN ? sl + W.s_H : sl + W.s_O; g.lda = d.n_mid(l);
     g.B = p.w_out; g.ldb = d.n_mid(l);
     g.C = ws() + W.P[sb]; g.ldc = d.h;
-    return gemm(KC_GEMM_FWD, KC, KC, EPI_STORE, g, c->cs);
+    return gemm(KC_GEMM_FWD, KC, KC, EPI_STORE, g, cst(sb));
   }
 
   int op_F(int l, int sb) {
-    if (overlap && l > 0) HIPX(hipStreamWaitEvent(c->cs, c->evCF[(l - 1) * 2 + sb], 0));
+    if (overlap && l > 0) HIPX(hipStreamWaitEvent(cst(sb), c->evCF[(l - 1) * 2 + sb], 0));
     const bool keep = mode == OASES_SERIAL_NO_RECOMPUTE;
     if (int r = column_part(l, sb, keep)) return r;
     if (int r = row_part(l, sb)) return r;
-    if (overlap) HIPX(hipEventRecord(c->evF[l * 2 + sb], c->cs));
+    if (overlap) HIPX(hipEventRecord(c->evF[l * 2 + sb], cst(sb)));
     return OASES_OK;
   }
   int op_CF(int l, int sb) {
-    hipStream_t s = overlap ? c->ss : c->cs;
+    hipStream_t s = overlap ? c->ss : cst(sb);
     if (overlap) HIPX(hipStreamWaitEvent(s, c->evF[l * 2 + sb], 0));
     if (int r = sum(ws() + W.P[sb], D().w > 1 ? peers(c->buf.peers_fwd, l, sb) : nullptr,
                     layer_out(l, sb), s, D().full ? tail(l, sb) : DropRes{}))
@@ -402,47 +409,47 @@ struct Exec {
     return OASES_OK;
   }
   int op_CR(int l, int sb) {
-    return sum(ws() + W.P[sb], D().w > 1 ? peers(c->buf.peers_fwd, l, sb) : nullptr, ws() + W.cr_out, c->cs,
+    return sum(ws() + W.P[sb], D().w > 1 ? peers(c->buf.peers_fwd, l, sb) : nullptr, ws() + W.cr_out, cst(sb),
                D().full ? tail(l, sb) : DropRes{});
   }
   int op_BdX(int l, int sb) {
     const Dims &d = D();
     const oases_layer_params &p = c->prm[l];
-    if (overlap && l < d.L - 1) HIPX(hipStreamWaitEvent(c->cs, c->evCB[(l + 1) * 2 + sb], 0));
+    if (overlap && l < d.L - 1) HIPX(hipStreamWaitEvent(cst(sb), c->evCB[(l + 1) * 2 + sb], 0));
     char *sl = slot(l, sb);
     const void *dy = dP(l, sb);
     if (d.full)  // the AllReduce inputs' gradient: dropout backward of dY (Eq. (1))
-      HIPX(dropout_bwd(grad_out(l, sb), ws() + W.dS[sb], (int64_t)d.T * d.h, tail(l, sb), c->cs));
+      HIPX(dropout_bwd(grad_out(l, sb), ws() + W.dS[sb], (int64_t)d.T * d.h, tail(l, sb), cst(sb)));
     char *dpre = ws() + W.dpre[sb];
     if (d.blocks[l] == OASES_FFN) {
       GemmArgs g{};  // dU = (dY W_out) * gelu'(U)
       g.M = d.T; g.N = d.fs; g.K = d.h;
       g.A = dy; g.lda = d.h; g.B = p.w_out; g.ldb = d.fs;
       g.C = dpre; g.ldc = d.fs; g.aux = sl + W.s_U; g.ld_aux = d.fs;
-      if (int r = gemm(KC_GEMM_DX, KC, MC, d.tanh ? EPI_GELU_BWD_TANH : EPI_GELU_BWD, g, c->cs)) return r;
+      if (int r = gemm(KC_GEMM_DX, KC, MC, d.tanh ? EPI_GELU_BWD_TANH : EPI_GELU_BWD, g, cst(sb))) return r;
     } else {
       GemmArgs g{};  // dO = dY W_o
       g.M = d.T; g.N = d.a; g.K = d.h;
       g.A = dy; g.lda = d.h; g.B = p.w_out; g.ldb = d.a;
       g.C = ws() + W.dO[sb]; g.ldc = d.a;
-      if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_STORE, g, c->cs)) return r;
-      if (int r = prof_begin(KC_ATTN_BWD, c->cs)) return r;
+      if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_STORE, g, cst(sb))) return r;
+      if (int r = prof_begin(KC_ATTN_BWD, cst(sb))) return r;
       HIPX(attention_bwd(d.nb, d.s, d.ns, d.d, d.causal, sl + W.s_QKV, sl + W.s_O, ws() + W.dO[sb],
                          reinterpret_cast<const float *>(sl + W.s_LSE),
-                         reinterpret_cast<float *>(ws() + W.delta[sb]), dpre, c->cs));
-      if (int r = prof_end(KC_ATTN_BWD, c->cs)) return r;
+                         reinterpret_cast<float *>(ws() + W.delta[sb]), dpre, cst(sb)));
+      if (int r = prof_end(KC_ATTN_BWD, cst(sb))) return r;
     }
     GemmArgs g{};  // dX_own = dpre W_in
     g.M = d.T; g.N = d.h; g.K = d.n_in(l);
     g.A = dpre; g.lda = d.n_in(l); g.B = p.w_in; g.ldb = d.h;
     g.C = ws() + W.dxo[sb]; g.ldc = d.h;
-    if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_STORE, g, c->cs)) return r;
-    if (overlap) HIPX(hipEventRecord(c->evBdX[l * 2 + sb], c->cs));
+    if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_STORE, g, cst(sb))) return r;
+    if (overlap) HIPX(hipEventRecord(c->evBdX[l * 2 + sb], cst(sb)));
     return OASES_OK;
   }
   int op_CB(int l, int sb) {
     const Dims &d = D();
-    hipStream_t s = overlap ? c->ss : c->cs;
+    hipStream_t s = overlap ? c->ss : cst(sb);
     if (overlap) HIPX(hipStreamWaitEvent(s, c->evBdX[l * 2 + sb], 0));
     if (!d.full) {
       if (int r = sum(ws() + W.dxo[sb], d.w > 1 ? peers(c->buf.peers_bwd, l, sb) : nullptr, grad_in(l, sb), s))
@@ -453,14 +460,24 @@ struct Exec {
                       DropRes{}, false))
         return r;
       const oases_layer_params &p = c->prm[l];
+      // the sub-batches' LayerNorm weight gradients accumulate in a fixed order
+      if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(s, c->evSB[d.L + l], 0));
       HIPX(layer_norm_bwd(ws() + W.dZ[sb], layer_in(l, sb), p.ln_w, grad_out(l, sb), grad_in(l, sb),
-                          reinterpret_cast<float *>(ws() + W.lnst[sb]), reinterpret_cast<float *>(ws() + W.lnpart),
+                          reinterpret_cast<float *>(ws() + W.lnst[sb]), reinterpret_cast<float *>(ws() + W.lnpart[sb]),
                           static_cast<float *>(p.dln_w), static_cast<float *>(p.dln_b), d.T, d.h, d.eps, sb, s));
     }
     if (overlap) HIPX(hipEventRecord(c->evCB[l * 2 + sb], s));
+    if (by_sb && sb == 0) HIPX(hipEventRecord(c->evSB[d.L + l], s));
     return OASES_OK;
   }
   int op_BdW(int l, int sb) {
+    // the two sub-batches' weight gradients accumulate in a fixed order
+    if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(c->ss, c->evSB[l], 0));
+    if (int r = weight_grads(l, sb)) return r;
+    if (by_sb && sb == 0) HIPX(hipEventRecord(c->evSB[l], c->cs));
+    return OASES_OK;
+  }
+  int weight_grads(int l, int sb) {
     const Dims &d = D();
     const oases_layer_params &p = c->prm[l];
     char *sl = slot(l, sb);
@@ -472,20 +489,20 @@ struct Exec {
     g.A = dy; g.lda = d.h;
     g.B = d.blocks[l] == OASES_FFN ? sl + W.s_H : sl + W.s_O; g.ldb = nmid;
     g.C = p.dw_out; g.ldc = nmid; g.beta = sb;
-    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g, c->cs)) return r;
+    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g, cst(sb))) return r;
     GemmArgs g2{};  // dW_in[nin, h] (+)= dpre^T X
     g2.M = nin; g2.N = d.h; g2.K = d.T;
     g2.A = dpre; g2.lda = nin; g2.B = gemm_in(l, sb); g2.ldb = d.h;
     g2.C = p.dw_in; g2.ldc = d.h; g2.beta = sb;
     if (bf16()) {  // db_in (+)= column sums of dpre, computed by the same GEMM
       g2.colsum = static_cast<float *>(p.db_in);
-      return gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, c->cs);
+      return gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, cst(sb));
     }
-    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, c->cs)) return r;
-    if (int r = prof_begin(KC_COLSUM, c->cs)) return r;
-    HIPX(colsum(bf16(), dpre, d.T, nin, nin, reinterpret_cast<float *>(ws() + W.colsum),
-                static_cast<float *>(p.db_in), sb, c->cs));
-    return prof_end(KC_COLSUM, c->cs);
+    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, cst(sb))) return r;
+    if (int r = prof_begin(KC_COLSUM, cst(sb))) return r;
+    HIPX(colsum(bf16(), dpre, d.T, nin, nin, reinterpret_cast<float *>(ws() + W.colsum[sb]),
+                static_cast<float *>(p.db_in), sb, cst(sb)));
+    return prof_end(KC_COLSUM, cst(sb));
   }
 
   int run(const Op &o) {
@@ -517,8 +534,9 @@ int Exec::gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmA
 int ensure_events(oases_ctx *c) {
   if (!c->evF.empty()) return OASES_OK;
   const int n = c->D.L * 2;
-  for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB}) {
-    v->resize(n, nullptr);
+  c->evSB.resize(n + 2, nullptr);
+  for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB, &c->evSB}) {
+    if (v != &c->evSB) v->resize(n, nullptr);
     // device-internal ordering only: no timing, no system-scope fence
     for (auto &e : *v) HIPX(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence));
   }
@@ -539,11 +557,21 @@ int issue_ops(oases_ctx *c, int mode, const std::vector<Op> &ops) {
   const WsLayout W = make_layout(c->D, mode);
   Exec ex{c, W, mode, mode == OASES_OVERLAP_FINE && c->ss != c->cs};
   ex.fused = mode == OASES_OVERLAP_FUSED && c->D.dtype == OASES_BF16;
+  ex.by_sb = mode == OASES_OVERLAP_STREAMS && c->ss != c->cs;
+  const int L = c->D.L;
+  if (ex.by_sb) {  // fork: the side stream starts after what precedes the step on the compute stream
+    HIPX(hipEventRecord(c->evSB[2 * L], c->cs));
+    HIPX(hipStreamWaitEvent(c->ss, c->evSB[2 * L], 0));
+  }
   for (const Op &o : ops)
     if (int r = ex.run(o)) return r;
   if (int r = ex.flush_pending()) return r;
   if (ex.overlap) {  // join the side stream into the compute stream
     HIPX(hipStreamWaitEvent(c->cs, c->evCB[0 * 2 + 1], 0));
+  }
+  if (ex.by_sb) {  // join
+    HIPX(hipEventRecord(c->evSB[2 * L + 1], c->ss));
+    HIPX(hipStreamWaitEvent(c->cs, c->evSB[2 * L + 1], 0));
   }
   return OASES_OK;
 }
@@ -576,7 +604,7 @@ int oases_create(const oases_config *cfg, oases_ctx **out) {
 
 int oases_workspace_bytes(const oases_config *cfg, int32_t mode, size_t *bytes) {
   if (!bytes) return OASES_E_ARG;
-  if (mode < 0 || mode > 4) return OASES_E_ARG;
+  if (mode < 0 || mode > 5) return OASES_E_ARG;
   Dims d;
   if (int r = check_config(cfg, &d, nullptr)) return r;
   *bytes = make_layout(d, mode).total;
@@ -679,7 +707,7 @@ int layer_bwd_recompute(oases_ctx *c, int32_t layer, int32_t sub_batch) {
 
 int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph) {
   if (!c) return OASES_E_ARG;
-  if (mode < 0 || mode > 4) return set_err(c, OASES_E_ARG, "bad mode");
+  if (mode < 0 || mode > 5) return set_err(c, OASES_E_ARG, "bad mode");
   if (int r = need_ready(c, mode)) return r;
   const std::vector<Op> ops = build_ops(c->D.L, mode);
   std::fill(c->fwd_done.begin(), c->fwd_done.end(), 0);
@@ -708,7 +736,7 @@ int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph) {
 
 int oases_schedule_ops(const oases_ctx *c, int32_t mode, int32_t *ops, int32_t cap, int32_t *n_ops) {
   if (!c || !n_ops || (cap > 0 && !ops) || cap < 0) return OASES_E_ARG;
-  if (mode < 0 || mode > 4) return OASES_E_ARG;
+  if (mode < 0 || mode > 5) return OASES_E_ARG;
   const std::vector<Op> v = build_ops(c->D.L, mode);
   *n_ops = (int32_t)v.size();
   for (int i = 0; i < (int)v.size() && i < cap; ++i) {
@@ -731,7 +759,7 @@ const char *oases_last_error(const oases_ctx *c) { return c ? c->err.c_str() : "
 void oases_destroy(oases_ctx *c) {
   if (!c) return;
   destroy_graphs(c);
-  for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB, &c->prof_ev})
+  for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB, &c->evSB, &c->prof_ev})
     for (auto &e : *v)
       if (e) (void)hipEventDestroy(e);
   delete c;

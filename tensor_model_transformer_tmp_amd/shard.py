@@ -20,7 +20,7 @@ OK, E_ARG, E_STATE, E_SHAPE, E_ALIGN, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3, -4, 
 F32, BF16 = 0, 1
 ATTN, FFN = 0, 1
 MODES = {"overlap_fine": 0, "serial_fine": 1, "serial_default": 2, "serial_norecompute": 3,
-         "overlap_fused": 4}
+         "overlap_fused": 4, "overlap_streams": 5}
 OP_KINDS = ("F", "C_F", "R", "C_R", "B_dX", "C_B", "B_dW")
 KCLASS = {"gemm_fwd": 0, "gemm_dx": 1, "gemm_dw": 2, "attn_fwd": 3, "attn_bwd": 4, "sum": 5,
           "colsum": 6}

@@ -26,15 +26,17 @@ if gpu_available():
 TOL = 2e-2
 
 CASES = [("c2_pair_h1024", False), ("c2_pair_h1024", True), ("c3_pair_h4096", False),
-         ("c3_pair_h4096", True), ("c4_stack8_h2048", True), ("c5_pair_h8192", True)]
+         ("c3_pair_h4096", True), ("c4_stack8_h2048", True), ("c5_pair_h8192", True),
+         ("c2_full_h1024", False), ("c2_full_h1024", True)]
 
 
 def _compare(cfg, got, ref):
     dec = lambda a: gen.storage_to_f64(a, cfg.dtype)
     assert_close(dec(got["Y"]), ref["Y"], TOL, f"{cfg.name} Y")
     assert_close(dec(got["dX"]), ref["dX"], TOL, f"{cfg.name} dX")
+    names = ("dw_in", "db_in", "dw_out") + (("dln_w", "dln_b") if cfg.full_block else ())
     for l in range(cfg.n_layers):
-        for n in ("dw_in", "db_in", "dw_out"):
+        for n in names:
             assert_close(got["grads"][l][n], ref["grads"][l][n], TOL, f"{cfg.name} layer {l} {n}")
 
 
@@ -49,14 +51,15 @@ def _bitwise_equal(a, b, what):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,zero_peers", CASES)
 def test_full_size_step_matches_oracle(name, zero_peers):
-    cfg = gen.PRESETS[name]
+    cfg = gen.PRESETS[name] if name in gen.PRESETS else gen.FULL_PRESETS[name]
     inp = gen.make_inputs(cfg, zero_peers=zero_peers)
     print(f"\n[{name} zero_peers={zero_peers}] device step", flush=True)
-    dev = DeviceShard(inp, modes=("overlap_fine", "overlap_fused", "serial_fine"))
+    dev = DeviceShard(inp, modes=("overlap_fine", "overlap_fused", "overlap_streams", "serial_fine"))
     dev.step("overlap_fine", use_graph=False)
     got = dev.results()
     for mode, graph in (("overlap_fine", True), ("overlap_fine", True), ("overlap_fused", False),
-                        ("overlap_fused", True), ("overlap_fused", True), ("serial_fine", False)):
+                        ("overlap_fused", True), ("overlap_fused", True), ("overlap_streams", False),
+                        ("overlap_streams", True), ("overlap_streams", True), ("serial_fine", False)):
         dev.step(mode, use_graph=graph)
         _bitwise_equal(dev.results(), got, f"{name} {mode} graph={graph}")
     dev.close()

@@ -15,7 +15,8 @@ if gpu_available():
     import torch
     from tensor_model_transformer_tmp_amd.device import DeviceShard
 
-MODES = ("overlap_fine", "overlap_fused", "serial_fine", "serial_default", "serial_norecompute")
+MODES = ("overlap_fine", "overlap_fused", "overlap_streams", "serial_fine", "serial_default",
+         "serial_norecompute")
 
 # small bf16 stacks with ragged sizes (tokens, hidden, heads and widths that do
 # not fill a tile) and both head sizes
