@@ -105,24 +105,33 @@ def class_work(cfg, kclass):
 
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """The float64 oracle step on this host (a bounded number of whole steps)."""
+def cpu_baseline(cfg, budget_s=12.0, budget_f32_s=4.0):
+    """The float64 oracle step on this host (a bounded number of whole steps),
+    and the same oracle run in float32 (reported beside it)."""
+    import numpy as np
     from oracle import schedule
     inp = gen.make_inputs(cfg)
     flops = sum(step_flops(cfg))
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        schedule.run_step(inp, "serial_fine")
-        n += 1
-        if time.perf_counter() - t0 >= budget_s or n >= 200:
-            break
-    dt = (time.perf_counter() - t0) / n
+
+    def timed(dtype, budget):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            schedule.run_step(inp, "serial_fine", work_dtype=dtype)
+            n += 1
+            if time.perf_counter() - t0 >= budget or n >= 200:
+                return n, (time.perf_counter() - t0) / n
+
+    n, dt = timed(np.float64, budget_s)
+    n32, dt32 = timed(np.float32, budget_f32_s)
     cores = len(os.sched_getaffinity(0))
+    blas = os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or "default"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} whole fp64 oracle steps of the {cfg.name} workload "
                       f"(serial fine-grained schedule), {dt:.2f} s per step, numpy/OpenBLAS "
-                      f"on {cores} threads"}
+                      f"on {cores} cores (BLAS threads: {blas})",
+            "fp32_value": flops / dt32 / 1e12,
+            "fp32_sample": f"{n32} whole oracle steps in float32, {dt32:.2f} s per step"}
 
 
 def stored_traffic(kclass, workload):

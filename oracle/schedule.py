@@ -80,27 +80,31 @@ class _Memory(dict):
         return self[key]
 
 
-def run_step(inp, mode: str, keep_trace: bool = False, keep_dy: bool = False):
+def run_step(inp, mode: str, keep_trace: bool = False, keep_dy: bool = False, work_dtype=np.float64):
     """Simulate one step of ``mode`` over the inputs ``inp`` (gen.ShardInputs).
 
     Returns a dict with Y [B*s, h], dX [B*s, h] (gradient w.r.t. the stack
     input), per-layer grads dw_in / db_in / dw_out, and the set of tensors
-    stored between the forward and the backward pass.
+    stored between the forward and the backward pass.  ``work_dtype``
+    float32 runs the same arithmetic in float32 (timing and diagnosis only;
+    the reference is float64).
     """
     cfg = inp.cfg
     L, T, nb = cfg.n_layers, cfg.t_sb, cfg.micro_batch // 2
     nh, d, s = cfg.heads_per_shard, cfg.head_dim, cfg.seq
-    x_all, g_all = inp.f64("x"), inp.f64("g")
-    w_in = [inp.f64("w_in", l) for l in range(L)]
-    b_in = [inp.f64("b_in", l) for l in range(L)]
-    w_out = [inp.f64("w_out", l) for l in range(L)]
+    f = lambda name, l=None: inp.f64(name, l).astype(work_dtype, copy=False)
+    x_all, g_all = f("x"), f("g")
+    w_in = [f("w_in", l) for l in range(L)]
+    b_in = [f("b_in", l) for l in range(L)]
+    w_out = [f("w_out", l) for l in range(L)]
     full = cfg.full_block
-    ln_w = [inp.f64("ln_w", l) for l in range(L)] if full else None
-    ln_b = [inp.f64("ln_b", l) for l in range(L)] if full else None
+    ln_w = [f("ln_w", l) for l in range(L)] if full else None
+    ln_b = [f("ln_b", l) for l in range(L)] if full else None
 
     def peers(kind, l, sb):
         src = inp.peers_fwd if kind == "fwd" else inp.peers_bwd
-        return [storage_to_f64(src[l, sb, k], cfg.dtype) for k in range(cfg.tmp_width - 1)]
+        return [storage_to_f64(src[l, sb, k], cfg.dtype).astype(work_dtype, copy=False)
+                for k in range(cfg.tmp_width - 1)]
 
     mem = _Memory()
     for sb in (0, 1):
