@@ -4,9 +4,9 @@ A step is one pass of the whole hot path over one micro-batch of seeded
 synthetic input: forward of every block for both sub-batches with the
 AllReduce-point sums overlapping the other sub-batch's compute, then the
 fine-grained recompute and backward of every block (Oases overlapped
-schedule).  The overlap is realised either with a side stream and events or
-by running each sum on extra workgroups of the next GEMM launch; each
-eagerly or as one hipGraph.  The fastest of the four is timed.
+schedule).  The overlap is realised with a side stream and events, by running
+each sum on extra workgroups of the next GEMM launch, or with one stream per
+sub-batch; each eagerly or as one hipGraph.  The fastest of the six is timed.
 
 Prints one JSON line.  ``value`` is the counted (algorithmic) TFLOP/s of the
 step; the roofline entry is for the kernel class with the most time per
@@ -219,6 +219,65 @@ def study_ablation(cfg, steps, warmup):
             "warmup": warmup, "modes": out}
 
 
+def event_timeline(dev, mode, steps):
+    """``steps`` eager steps of ``mode`` with every kernel-class launch timed
+    by HIP events carried in its dispatch packets: (figures, text chart) of
+    how the launches ran side by side (no profiler attached)."""
+    from tensor_model_transformer_tmp_amd.rocprof_summary import overlap_report
+    import torch
+    cap = 16384
+    dev.ctx.profile_begin("all", cap)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dev.ctx.schedule_step(mode, False)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    rows = [(a * 1e6, b * 1e6, ("compute", "side", "other")[st], cls, cls)
+            for cls, st, a, b in dev.ctx.profile_timeline(cap)]
+    fig, text = overlap_report(rows, steps)
+    fig["ms_per_step_with_events"] = t * 1e3
+    return fig, text
+
+
+def _plain_ms(dev, mode, steps):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dev.ctx.schedule_step(mode, False)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def study_trace(cfg, mode, steps, warmup, timeline_out=None):
+    """Steps of one schedule only, issued eagerly, for a kernel trace: warm-up
+    and timed steps are all the library runs, so a rocprofv3 kernel trace of
+    this command is a timeline of exactly those steps (the trace summary
+    measures how much of each AllReduce-point sum ran beside compute
+    kernels).  Then the same number of steps again with dispatch-packet
+    events on every launch, for the same figures without a profiler."""
+    import torch
+    from tensor_model_transformer_tmp_amd.device import DeviceShard
+
+    dev = DeviceShard(gen.make_inputs(cfg), device="cuda:0", modes=(mode,))
+    for _ in range(warmup):
+        dev.ctx.schedule_step(mode, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dev.ctx.schedule_step(mode, False)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / steps
+    fig, text = event_timeline(dev, mode, steps)
+    dev.close()
+    if timeline_out:
+        with open(timeline_out, "w") as fh:
+            fh.write(f"{cfg.name}, {mode} eager, HIP events in every launch's dispatch packets\n"
+                     + text + "\n")
+    return {"study": "trace", "workload": cfg.name, "schedule": mode + "+eager", "steps": steps,
+            "warmup": warmup, "ms_per_step": t * 1e3, "event_timeline": fig}
+
+
 def _layer_gemms(cfg, l, T):
     """The six GEMMs of block l over T tokens: (name, a_layout, b_layout, M, N, K)."""
     h, nin, nmid = cfg.hidden, cfg.n_in(l), cfg.n_mid(l)
@@ -303,9 +362,15 @@ def main():
                     help="kernel class for the roofline entry (default: most time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES three times (counter calibration)")
-    ap.add_argument("--study", choices=("ablation", "density"), default=None,
+    ap.add_argument("--study", choices=("ablation", "density", "trace"), default=None,
                     help="run a study instead of the timed step: schedule ablation on --config, "
-                         "or the batch-split GEMM density study over the bf16 workloads")
+                         "the batch-split GEMM density study over the bf16 workloads, or "
+                         "--steps eager steps of --schedule alone (for a kernel trace)")
+    ap.add_argument("--schedule", default="overlap_streams",
+                    choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
+                    help="schedule of --study trace")
+    ap.add_argument("--timeline-out", default=None, metavar="PATH",
+                    help="--study trace: write the event timeline's text chart here")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
@@ -317,6 +382,10 @@ def main():
 
     if args.study == "ablation":
         print(json.dumps(study_ablation(_preset(args.config), args.steps, args.warmup)), flush=True)
+        return 0
+    if args.study == "trace":
+        print(json.dumps(study_trace(_preset(args.config), args.schedule, args.steps, args.warmup,
+                                     args.timeline_out)), flush=True)
         return 0
     if args.study == "density":
         names = [n for n in gen.PRESET_ORDER if gen.PRESETS[n].dtype == gen.BF16]
@@ -366,6 +435,18 @@ def main():
         run("overlap_fine", False, steps)
         ms, n = dev.ctx.profile_end()
         return ms / 1e3, n
+
+    # how much of the sums' time ran beside compute kernels, from one event
+    # timeline of the timed schedule (eager; a fused sum has no launch of its own)
+    # The events cost time per launch; where they slow the step by more than
+    # 15% (small workloads, many short launches) the timeline no longer shows
+    # the uninstrumented overlap and its figure is not reported.
+    tl_mode = "overlap_streams" if mode == "overlap_fused" else mode
+    tl_fig, _ = event_timeline(dev, tl_mode, 5)
+    tl_fig["schedule"] = tl_mode + "+eager"
+    tl_fig["ms_per_step_plain"] = _plain_ms(dev, tl_mode, 5)
+    tl_fig["instrumented_over_plain"] = tl_fig["ms_per_step_with_events"] / tl_fig["ms_per_step_plain"]
+    beside = tl_fig["hidden_frac"] if tl_fig["instrumented_over_plain"] <= 1.15 else None
 
     prof_steps = max(3, min(args.steps, 20))
     kernels = {}
@@ -420,6 +501,8 @@ def main():
                       if cfg.full_block else {})},
         "mfma_peak_frac": value / MFMA_BF16_PEAK_TFLOPS,
         "reduction_hidden_frac": hidden,
+        "reduction_beside_compute_frac": beside,
+        "event_timeline": tl_fig,
         "serial_ms_per_step": sec_serial * 1e3,
         "launch_probe_ms": {f"{m}+{'graph' if g else 'eager'}": t * 1e3 for (m, g), t in launch.items()},
         "sum_ms_per_step": sum_per_step * 1e3,

@@ -227,9 +227,18 @@ void oases_destroy(oases_ctx *c);
  * from the start of its first kernel to the end of its last, on the stream
  * it is launched on.  oases_profile_end waits for those events and returns
  * the summed time and the number of launches timed.  Timing state is per
- * host thread. */
+ * host thread.  kernel_class 7 times every class.
+ * oases_profile_timeline ends a timing run like oases_profile_end but
+ * returns each timed launch: its class, its stream (0 the compute stream,
+ * 1 the side stream, 2 another) and the start and end of its kernels in ms
+ * after the start of the first timed launch (all streams share the GPU's
+ * clock), in launch order.  classes, streams, start_ms and end_ms are caller
+ * arrays of cap entries; more timed launches than cap is OASES_E_ARG (the
+ * run stays open).  Blocks the host until the timed launches have ended. */
 int oases_profile_begin(oases_ctx *c, int32_t kernel_class, int32_t max_launches);
 int oases_profile_end(oases_ctx *c, double *total_ms, int32_t *launches);
+int oases_profile_timeline(oases_ctx *c, int32_t cap, int32_t *classes, int32_t *streams, double *start_ms,
+                           double *end_ms, int32_t *launches);
 
 /* ---- single-kernel entry points (used by tests and the benchmark) ----
  * They run one kernel family on `stream` (NULL = default) with the same
@@ -263,8 +272,9 @@ int oases_gemm(int32_t dtype, int32_t a_layout, int32_t b_layout, int32_t epilog
                int32_t beta, void *stream);
 
 /* Tile configuration of the bf16 GEMMs for this process: 0 = automatic (the
- * default), 1..19 force one of the compiled tile shapes and pipeline depths
- * (tests and tuning sweeps).  Returns OASES_E_ARG for other values. */
+ * default), 1..22 force one of the compiled tile shapes and pipeline depths
+ * (tests and tuning sweeps; 20..22 split each tile's k loop between two wave
+ * groups, or run their tile with one group where the k-tile count is odd).  Returns OASES_E_ARG for other values. */
 int oases_gemm_tile_variant(int32_t variant);
 
 /* Largest number of workgroups of the AllReduce-point sum kernel for this

@@ -214,8 +214,10 @@ struct oases_ctx {
   std::vector<uint8_t> fwd_done, bwd_done;
   std::string err;
   // timing instrumentation
-  int prof_class = -1;
+  int prof_class = -1;  // KC_COUNT: every class
   std::vector<hipEvent_t> prof_ev;
+  std::vector<int32_t> prof_cls;  // class of each timed launch (event pair)
+  std::vector<int32_t> prof_str;  // its stream: 0 compute, 1 side, 2 other
   size_t prof_used = 0;
   bool capturing = false;
 };
@@ -306,17 +308,24 @@ struct Exec {
 
   // Time one launch of kernel class `cls`: arm the next event pair, which the
   // kernels launched until prof_end carry in their dispatch packets.
+  bool profiled(int cls) const {
+    return (c->prof_class == cls || c->prof_class == KC_COUNT) && !c->capturing;
+  }
   int prof_begin(int cls, hipStream_t) {
-    if (c->prof_class != cls || c->capturing) return OASES_OK;
+    if (!profiled(cls)) return OASES_OK;
     if (c->prof_used + 2 > c->prof_ev.size()) return OASES_OK;  // ring full: stop timing
     launch_timer() = LaunchTimer{c->prof_ev[c->prof_used], c->prof_ev[c->prof_used + 1]};
     return OASES_OK;
   }
-  int prof_end(int cls, hipStream_t) {
-    if (c->prof_class != cls || c->capturing) return OASES_OK;
+  int prof_end(int cls, hipStream_t s) {
+    if (!profiled(cls)) return OASES_OK;
     const bool launched = launch_timer().stop && !launch_timer().start;  // a kernel took the pair
     launch_timer() = LaunchTimer{};
-    if (launched) c->prof_used += 2;
+    if (launched) {
+      c->prof_cls[c->prof_used / 2] = cls;
+      c->prof_str[c->prof_used / 2] = s == c->cs ? 0 : (s == c->ss ? 1 : 2);
+      c->prof_used += 2;
+    }
     return OASES_OK;
   }
 
@@ -769,10 +778,12 @@ void oases_destroy(oases_ctx *c) {
 
 int oases_profile_begin(oases_ctx *c, int32_t kernel_class, int32_t max_launches) {
   if (!c) return OASES_E_ARG;
-  if (kernel_class < 0 || kernel_class >= KC_COUNT || max_launches < 1 || max_launches > 1 << 16)
+  if (kernel_class < 0 || kernel_class > KC_COUNT || max_launches < 1 || max_launches > 1 << 16)
     return set_err(c, OASES_E_ARG, "bad kernel class or launch count");
   for (auto &e : c->prof_ev) if (e) (void)hipEventDestroy(e);
   c->prof_ev.assign((size_t)max_launches * 2, nullptr);
+  c->prof_cls.assign((size_t)max_launches, -1);
+  c->prof_str.assign((size_t)max_launches, -1);
   for (auto &e : c->prof_ev) HIPX(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   c->prof_used = 0;
   c->prof_class = kernel_class;
@@ -791,6 +802,29 @@ int oases_profile_end(oases_ctx *c, double *total_ms, int32_t *launches) {
   }
   *total_ms = tot;
   *launches = (int32_t)(c->prof_used / 2);
+  c->prof_class = -1;
+  c->prof_used = 0;
+  launch_timer() = LaunchTimer{};
+  return OASES_OK;
+}
+
+int oases_profile_timeline(oases_ctx *c, int32_t cap, int32_t *classes, int32_t *streams, double *start_ms,
+                           double *end_ms, int32_t *launches) {
+  if (!c || !launches || cap < 0 || (cap > 0 && (!classes || !streams || !start_ms || !end_ms)))
+    return OASES_E_ARG;
+  const size_t n = c->prof_used / 2;
+  if (n > (size_t)cap) return set_err(c, OASES_E_ARG, "timeline buffers hold fewer launches than were timed");
+  for (size_t i = 0; i < n; ++i) {
+    HIPX(hipEventSynchronize(c->prof_ev[2 * i + 1]));
+    float a = 0, b = 0;
+    HIPX(hipEventElapsedTime(&a, c->prof_ev[0], c->prof_ev[2 * i]));
+    HIPX(hipEventElapsedTime(&b, c->prof_ev[0], c->prof_ev[2 * i + 1]));
+    classes[i] = c->prof_cls[i];
+    streams[i] = c->prof_str[i];
+    start_ms[i] = a;
+    end_ms[i] = b;
+  }
+  *launches = (int32_t)n;
   c->prof_class = -1;
   c->prof_used = 0;
   launch_timer() = LaunchTimer{};
@@ -864,7 +898,7 @@ int oases_attention_variant(int32_t variant) {
 }
 
 int oases_gemm_tile_variant(int32_t variant) {
-  if (variant < 0 || variant > 19) return OASES_E_ARG;
+  if (variant < 0 || variant > 22) return OASES_E_ARG;
   gemm_bf16_set_variant(variant);
   return OASES_OK;
 }

@@ -317,10 +317,18 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, Layout LA, Layout LB, int EPI>
-__global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
+// KS k groups: the workgroup holds KS groups of WGM x WGN waves.  Group kg
+// walks k tiles [kg * nk, (kg + 1) * nk) of the nk * KS tiles (the host only
+// launches KS = 2 for an even tile count) through its own LDS ring, in step
+// with the other group (one shared barrier per k step), so a CU keeps twice
+// the operand bytes in flight for a tile of C.  Group 1 then hands its
+// partial tile to group 0 through LDS, which adds it to its own in a fixed
+// order (deterministic) and runs the epilogue.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int BK, int KS, Layout LA, Layout LB, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN * KS) gemm_bf16_kernel(GemmArgs g) {
   static_assert(STAGES >= 2 && STAGES <= 6, "2 to 6 stages");
-  constexpr int NW = WGM * WGN;
+  static_assert(KS == 1 || KS == 2, "one or two k groups");
+  constexpr int NW = WGM * WGN;  // waves per k group
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1, "tile shape");
@@ -328,11 +336,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   using TB = Tile<BN, NW, LB, BK>;
   constexpr int DL = TA::PER_WAVE + TB::PER_WAVE;  // DMA instructions per wave per stage
   static_assert((STAGES - 2) * DL < 64, "vmcnt range");
-  static_assert(STAGES * (BM + BN) * BK * 2 <= 160 * 1024, "LDS");
-  // LDS ring of STAGES slots per operand, always indexed with compile-time
-  // slot numbers (fragment reads get immediate offsets)
-  __shared__ __attribute__((aligned(1024))) bf16_t sA[STAGES][BM * BK];
-  __shared__ __attribute__((aligned(1024))) bf16_t sB[STAGES][BN * BK];
+  static_assert(STAGES * KS * (BM + BN) * BK * 2 <= 160 * 1024, "LDS");
+  // LDS ring of STAGES slots per operand and k group, always indexed with
+  // compile-time slot numbers (fragment reads get immediate offsets from the
+  // group's base)
+  constexpr int A_ELEMS = STAGES * KS * BM * BK;  // the A ring, then the B ring
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * KS * (BM + BN) * BK];
 
   // the first g.sum.wgs workgroups run a fused AllReduce-point sum
   if ((int)blockIdx.x < g.sum.wgs) {
@@ -340,7 +349,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = KS == 1 ? 0 : wave_wg / NW;  // k group
+  const int wave = KS == 1 ? wave_wg : wave_wg % NW;  // wave within its group
   const int l32 = lane & 31, hl = lane >> 5;  // hl: which 32-lane half
   const int wm = wave % WGM, wn = wave / WGM;
 
@@ -360,17 +371,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
 
   const bf16_t *A = static_cast<const bf16_t *>(g.A);
   const bf16_t *B = static_cast<const bf16_t *>(g.B);
-  const int nk = (g.K + BK - 1) / BK;
+  const int nk = (g.K + BK - 1) / BK / KS;  // k tiles of this group
+  const int kt0 = kg * nk;                  // its first k tile
 
-  auto slotA = [&](auto I) -> bf16_t * { return sA[decltype(I)::value]; };
-  auto slotB = [&](auto I) -> bf16_t * { return sB[decltype(I)::value]; };
+  auto slotA = [&](auto I) -> bf16_t * { return smem + (decltype(I)::value * KS + kg) * BM * BK; };
+  auto slotB = [&](auto I) -> bf16_t * { return smem + A_ELEMS + (decltype(I)::value * KS + kg) * BN * BK; };
   TA ta;
   TB tb;
   ta.init(g.lda, m0, g.M, wave, lane);
   tb.init(g.ldb, n0, g.N, wave, lane);
   auto issue = [&](auto I, int stage) {
-    ta.issue(A, g.lda, m0, stage * BK, g.K, lds_addr(slotA(I)), wave, lane);
-    tb.issue(B, g.ldb, n0, stage * BK, g.K, lds_addr(slotB(I)), wave, lane);
+    ta.issue(A, g.lda, m0, (kt0 + stage) * BK, g.K, lds_addr(slotA(I)), wave, lane);
+    tb.issue(B, g.ldb, n0, (kt0 + stage) * BK, g.K, lds_addr(slotB(I)), wave, lane);
   };
   f32x16 acc[TN][TM];
   // column sums of A over k (bias gradient beside a weight gradient): every
@@ -417,8 +429,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
     read_frags(0, 0);
     // k substeps unrolled at compile time, so every fragment and accumulator
     // index is a constant before the register promotion of local arrays
-    static_for<0, BK / 16>([&](auto KS) {
-      constexpr int ks = decltype(KS)::value;
+    static_for<0, BK / 16>([&](auto KSUB) {
+      constexpr int ks = decltype(KSUB)::value;
       if constexpr (ks + 1 < BK / 16) read_frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
@@ -464,6 +476,40 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
     if (kt + decltype(I)::value < nk) step(I, kt + decltype(I)::value);
   });
 
+  if constexpr (KS == 2) {
+    // group 1's partial tile (and column sums) to group 0 through LDS; the
+    // ring is free once every wave has passed this barrier
+    constexpr int NT = NW * 64;  // threads of a group
+    static_assert((TN * TM * 16 + TM) * NT * 4 <= (int)sizeof(smem), "reduction buffer");
+    float *red = reinterpret_cast<float *>(smem);
+    const int t = wave * 64 + lane;
+    lds_barrier();
+    if (kg == 1) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((j * TM + i) * 16 + r) * NT + t] = acc[j][i][r];
+      if constexpr (COL) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) red[(TN * TM * 16 + i) * NT + t] = csum[i];
+      }
+    }
+    lds_barrier();
+    if (kg == 1) return;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] += red[((j * TM + i) * 16 + r) * NT + t];
+    if constexpr (COL) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) csum[i] += red[(TN * TM * 16 + i) * NT + t];
+    }
+  }
+
   // epilogue: acc[j][i][jj*4 + ii] is C[m][n] with
   //   m = m0 + wm*WTM + i*32 + l32,  n = n0 + wn*WTN + j*32 + jj*8 + hl*4 + ii
   int ncol[TN][4];
@@ -496,11 +542,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI, int BK = 64>
+template <int BM, int BN, int WGM, int WGN, int STAGES, Layout LA, Layout LB, int EPI, int BK = 64, int KS = 1>
 hipError_t launch(const GemmArgs &g, hipStream_t s) {
+  if constexpr (KS > 1) {  // k groups need an equal number of k tiles each
+    if (((g.K + BK - 1) / BK) % KS != 0) return launch<BM, BN, WGM, WGN, STAGES, LA, LB, EPI, BK, 1>(g, s);
+  }
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  OASES_LAUNCH((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, BK, LA, LB, EPI>), dim3(tiles + g.sum.wgs),
-                     dim3(64 * WGM * WGN), s, g);
+  OASES_LAUNCH((gemm_bf16_kernel<BM, BN, WGM, WGN, STAGES, BK, KS, LA, LB, EPI>), dim3(tiles + g.sum.wgs),
+                     dim3(64 * WGM * WGN * KS), s, g);
   return hipGetLastError();
 }
 
@@ -519,15 +568,26 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     // 64x64 tiles cover in at most two rounds run on 4-stage 64x64 tiles
     // (with the two sub-batches' GEMMs running side by side, the deeper ring
     // measured 5% faster over the 1024-hidden step).  Large weight gradients
-    // wider than they are tall run best on 2-stage 128x128.
+    // wider than they are tall run best on 2-stage 128x128.  Measured with
+    // two k groups (hipGraph replays): the 1024-hidden weight gradients
+    // (k = 2048 tokens) 12.2-13.2 -> 9.7-10.7 us, the 4096-hidden
+    // out-projection data gradient (2048x512, k = 4096) 24.2 -> 16.7 us.
     const int64_t t256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
     const int64_t t128x256 = (int64_t)((g.M + 127) / 128) * ((g.N + 255) / 256);
     const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
     const int64_t t64 = (int64_t)((g.M + 63) / 64) * ((g.N + 63) / 64);
+    const int64_t t64x128 = (int64_t)((g.M + 63) / 64) * ((g.N + 127) / 128);
     const bool wide_dw = LA == MC && g.M < g.N;
+    // long k loops over too few tiles for two workgroups per CU: two k groups
+    // per tile (an even k-tile count, at least 16) -- 64x64 tiles while they
+    // give at most one tile per CU, else 64x128 while those do
+    const int nk64 = (g.K + 63) / 64;
+    const bool ks2 = nk64 % 2 == 0 && nk64 >= 16;
     if (wide_dw && t128 >= 1024) v = 5;
     else if (t256 >= 256) v = 4;
     else if (t128x256 >= 192) v = 3;
+    else if (t128 < 256 && ks2 && t64 <= 256) v = 20;
+    else if (t128 < 256 && ks2 && t64x128 <= 256) v = 21;
     else if (t128 < 256 && g.K >= 4096) v = t128 >= 192 ? 13 : (wide_dw ? 12 : 9);
     else if (t128 < 256) v = t64 <= 512 ? 19 : (wide_dw ? 8 : 7);
     else if (g.K >= 2048) v = 2;
@@ -553,6 +613,10 @@ hipError_t dispatch_tile(const GemmArgs &g, hipStream_t s) {
     case 17: return launch<256, 128, 4, 2, 5, LA, LB, EPI, 32>(g, s);
     case 18: return launch<64, 64, 2, 2, 2, LA, LB, EPI>(g, s);
     case 19: return launch<64, 64, 2, 2, 4, LA, LB, EPI>(g, s);
+    // two k groups (an odd k-tile count runs the same tile with one group)
+    case 20: return launch<64, 64, 2, 2, 4, LA, LB, EPI, 64, 2>(g, s);
+    case 21: return launch<64, 128, 2, 2, 3, LA, LB, EPI, 64, 2>(g, s);
+    case 22: return launch<128, 128, 2, 2, 2, LA, LB, EPI, 64, 2>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

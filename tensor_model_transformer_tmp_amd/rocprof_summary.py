@@ -14,6 +14,16 @@ trace and a counter run can be set beside the event timings.
   python -m tensor_model_transformer_tmp_amd.rocprof_summary traffic-all --workload W \
       --outdir profiles ... (same inputs; one <class>_<W>_traffic.txt per class)
 
+  python -m tensor_model_transformer_tmp_amd.rocprof_summary timeline <kernel_trace.csv> --steps K --warmup W
+  python -m tensor_model_transformer_tmp_amd.rocprof_summary mfma <counter_collection.csv> [--workload W]
+
+``timeline`` reads a kernel trace of ``bench.py --study trace`` (W warm-up
+steps, then K plain steps of one schedule, then K with events), measures how much of every
+AllReduce-point sum ran while a compute kernel (GEMM or attention) was running
+on the GPU, and draws one step as a per-queue text chart.  ``mfma`` averages
+the MFMA busy fraction (``MfmaUtil``, weighted by each dispatch's active
+cycles) and the executed bf16 MFMA FLOPs per class launch.
+
 ``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
 same counters read for a plain copy of known size (the sum kernel with no
 peers), and prints the per-class-launch HBM bytes together with a hash of the
@@ -150,11 +160,182 @@ def traffic_lines(kernel, fetch_csv, write_csv, cf_csv, cw_csv, calib_bytes):
             f"sources_sha256: {sources_hash(kernel)}"]
 
 
+def _trace_rows(path: str):
+    """Kernel dispatches of a rocprofv3 kernel_trace.csv as
+    (start_ns, end_ns, queue, class or None, short name), sorted by start."""
+    with open(path, newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    names = _demangle(sorted({r["Kernel_Name"] for r in rows}))
+    out = []
+    for r in rows:
+        n = names[r["Kernel_Name"]]
+        short = re.sub(r"\(.*$", "", n.replace("(anonymous namespace)::", "").replace("oases::", ""))
+        short = re.sub(r"^void ", "", short)
+        q = r.get("Queue_Id") or r.get("Stream_Id") or "0"
+        out.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), q, kernel_class(n), short))
+    out.sort()
+    return out
+
+
+def _union_len(iv):
+    """Total length of the union of intervals [(a, b), ...]."""
+    tot, cur_a, cur_b = 0, None, None
+    for a, b in sorted(iv):
+        if cur_b is None or a > cur_b:
+            if cur_b is not None:
+                tot += cur_b - cur_a
+            cur_a, cur_b = a, b
+        else:
+            cur_b = max(cur_b, b)
+    return tot + (cur_b - cur_a if cur_b is not None else 0)
+
+
+_LETTER = {"gemm_fwd": "F", "gemm_dx": "X", "gemm_dw": "W", "attn_fwd": "a", "attn_bwd": "b",
+           "sum": "S", "colsum": "c"}
+
+
+def timed_trace_rows(path: str, steps: int, warmup: int):
+    """The classified dispatches of the plain timed steps of a kernel trace of
+    ``bench.py --study trace``, which runs ``warmup`` steps, ``steps`` plain
+    steps and ``steps`` steps with events on every launch, and nothing else
+    of the library: its classified dispatches are warmup + 2 steps equal steps."""
+    rows = [r for r in _trace_rows(path) if r[3] is not None]
+    per_step = len(rows) // (warmup + 2 * steps)
+    return rows[warmup * per_step:(warmup + steps) * per_step]
+
+
+def overlap_report(rows, steps: int, width: int = 120, unit: float = 1e3) -> tuple:
+    """(figures, text) for the dispatches of ``steps`` whole steps, given as
+    (start, end, queue, class, name) with times in ns (``unit`` = 1e3 per us).
+
+    hidden fraction = the part of the AllReduce-point sums' time during which
+    at least one compute kernel (any other class) was running on the GPU."""
+    rows = sorted(rows)
+    t0, t1 = rows[0][0], max(r[1] for r in rows)
+    sums = [r for r in rows if r[3] == "sum"]
+    compute = [(r[0], r[1]) for r in rows if r[3] != "sum"]
+    tot_sum = sum(r[1] - r[0] for r in sums)
+    covered = 0
+    for a, b, *_ in sums:
+        covered += _union_len([(max(a, c0), min(b, c1)) for c0, c1 in compute if c0 < b and c1 > a])
+    busy = _union_len([(r[0], r[1]) for r in rows])
+    qs = sorted({r[2] for r in rows})
+    per_step = len(rows) // max(steps, 1)
+    fig = {"steps": steps, "launches_per_step": per_step, "span_us_per_step": (t1 - t0) / unit / steps,
+           "sum_us_per_step": tot_sum / unit / steps, "sum_beside_compute_us_per_step": covered / unit / steps,
+           "hidden_frac": covered / tot_sum if tot_sum else None, "busy_frac": busy / (t1 - t0),
+           "kernel_time_over_span": sum(r[1] - r[0] for r in rows) / (t1 - t0)}
+    out = [f"timed steps: {steps}; timed launches: {len(rows)} ({per_step} per step) on "
+           f"{len(qs)} queue(s); span {fig['span_us_per_step']:.1f} us per step",
+           f"AllReduce-point sums: {len(sums)} launches, {fig['sum_us_per_step']:.1f} us per step; "
+           f"time during which a compute kernel was also running: "
+           f"{fig['sum_beside_compute_us_per_step']:.1f} us per step -> hidden fraction "
+           f"{fig['hidden_frac'] if fig['hidden_frac'] is not None else float('nan'):.3f}",
+           f"GPU busy (any kernel running): {fig['busy_frac']:.3f} of the span; "
+           f"sum of kernel durations / span: {fig['kernel_time_over_span']:.2f}",
+           ""]
+    # one step: the launches of the middle timed step (steps end with a join
+    # of the streams, so consecutive steps do not overlap)
+    k = steps // 2
+    step = rows[k * per_step:(k + 1) * per_step]
+    s0 = step[0][0]
+    span = max(max(r[1] for r in step) - s0, 1)
+    out.append(f"step {k}: {span / unit:.1f} us; one character = {span / width / unit:.2f} us; "
+               + ", ".join(f"{v} {c}" for c, v in _LETTER.items()) + ", . idle")
+    for q in qs:
+        line = ["."] * width
+        for a, b, qq, cls, _ in step:
+            if qq != q:
+                continue
+            i0 = int((a - s0) * width / span)
+            i1 = max(i0 + 1, int((b - s0) * width / span))
+            for i in range(i0, min(i1, width)):
+                line[i] = _LETTER.get(cls, "?")
+        out.append(f"queue {q!s:>3} |{''.join(line)}|")
+    out += ["", "start us | end us | queue | class | kernel", "---|---|---|---|---"]
+    for a, b, q, cls, n in step:
+        out.append(f"{(a - s0) / unit:.1f} | {(b - s0) / unit:.1f} | {q} | {cls} | {n[:80]}")
+    return fig, "\n".join(out)
+
+
+def timeline(path: str, steps: int, warmup: int, width: int = 120) -> str:
+    """Hidden-sum figures over the timed steps of a kernel trace and a text
+    chart of one step."""
+    rows = timed_trace_rows(path, steps, warmup)
+    if not rows:
+        return "no classified kernels in the trace"
+    return overlap_report(rows, steps, width)[1]
+
+
+def mfma_table(path: str, work=None) -> str:
+    """Per class: MFMA busy fraction (MfmaUtil weighted by GRBM_GUI_ACTIVE) and
+    executed bf16 MFMA FLOPs per class launch (MfmaFlopsBF16, or
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512).  ``work``: {class: algorithmic FLOPs
+    per class launch}, printed beside the executed figure when given."""
+    with open(path, newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    names = _demangle(sorted({r["Kernel_Name"] for r in rows}))
+    disp = defaultdict(dict)
+    for r in rows:
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Kernel_Name"])
+        disp[key][r["Counter_Name"]] = float(r["Counter_Value"])
+    util_w, act, flops = (defaultdict(float) for _ in range(3))
+    launches = defaultdict(int)
+    for (_, kname), c in disp.items():
+        n = names[kname]
+        cls = kernel_class(n)
+        if cls is None:
+            continue
+        a = c.get("GRBM_GUI_ACTIVE", 1.0)
+        if "MfmaUtil" in c:
+            util_w[cls] += c["MfmaUtil"] * a
+            act[cls] += a
+        flops[cls] += c.get("MfmaFlopsBF16", c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512)
+        if _is_lead(n, cls):
+            launches[cls] += 1
+    out = ["class | class launches | MFMA busy % | executed bf16 MFMA GFLOP per launch"
+           + (" | algorithmic GFLOP per launch | executed / algorithmic" if work else ""),
+           "---|---|---|---" + ("|---|---" if work else "")]
+    for cls in sorted(launches, key=lambda c: -flops[c]):
+        n = max(launches[cls], 1)
+        line = (f"{cls} | {launches[cls]} | {util_w[cls] / act[cls] if act[cls] else float('nan'):.1f} | "
+                f"{flops[cls] / n / 1e9:.3f}")
+        if work and cls in work and work[cls] > 0:
+            line += f" | {work[cls] / 1e9:.3f} | {flops[cls] / n / work[cls]:.3f}"
+        elif work:
+            line += " | - | -"
+        out.append(line)
+    return "\n".join(out)
+
+
+def _class_work_per_launch(workload: str):
+    """Algorithmic FLOPs per class launch of a named workload (bench.py's counts)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    import gen
+    cfg = gen.PRESETS[workload] if workload in gen.PRESETS else gen.FULL_PRESETS[workload]
+    out = {}
+    for kc in bench.KERNEL_CLASSES:
+        w, unit = bench.class_work(cfg, kc)
+        if unit == "FLOP" and w > 0:
+            out[kc] = w / bench.class_launches(cfg, kc)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    t = sub.add_parser("timeline")
+    t.add_argument("csv")
+    t.add_argument("--steps", type=int, required=True)
+    t.add_argument("--warmup", type=int, required=True)
+    t.add_argument("--width", type=int, default=120)
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("--workload", default=None)
     for name in ("traffic", "traffic-all"):
         t = sub.add_parser(name)
         if name == "traffic":
@@ -171,6 +352,12 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv))
+        return 0
+    if a.cmd == "timeline":
+        print(timeline(a.csv, a.steps, a.warmup, a.width))
+        return 0
+    if a.cmd == "mfma":
+        print(mfma_table(a.csv, _class_work_per_launch(a.workload) if a.workload else None))
         return 0
     args = (a.fetch, a.write, a.calib_fetch, a.calib_write, a.calib_bytes)
     if a.cmd == "traffic":

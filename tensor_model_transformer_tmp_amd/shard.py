@@ -23,12 +23,12 @@ MODES = {"overlap_fine": 0, "serial_fine": 1, "serial_default": 2, "serial_norec
          "overlap_fused": 4, "overlap_streams": 5}
 OP_KINDS = ("F", "C_F", "R", "C_R", "B_dX", "C_B", "B_dW")
 KCLASS = {"gemm_fwd": 0, "gemm_dx": 1, "gemm_dw": 2, "attn_fwd": 3, "attn_bwd": 4, "sum": 5,
-          "colsum": 6}
+          "colsum": 6, "all": 7}  # "all": every class (timeline runs)
 
 EXPORTED = ("oases_create", "oases_workspace_bytes", "oases_bind", "oases_set_streams",
             "layer_fwd", "layer_bwd_recompute", "schedule_step", "oases_schedule_ops",
             "oases_sync", "oases_last_error", "oases_destroy", "oases_profile_begin",
-            "oases_profile_end", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
+            "oases_profile_end", "oases_profile_timeline", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
             "oases_attention_variant", "oases_sum_grid_cap", "oases_attention_fwd")
 
 
@@ -81,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "oases_destroy": (None, [P]),
         "oases_profile_begin": (ctypes.c_int, [P, I32, I32]),
         "oases_profile_end": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
+        "oases_profile_timeline": (ctypes.c_int, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                                  ctypes.POINTER(ctypes.c_double),
+                                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
         "oases_allreduce_point": (ctypes.c_int, [I32, P, P, I64, I32, P, I64, P]),
         "oases_gemm": (ctypes.c_int, [I32, I32, I32, I32, I32, I32, I32, P, I32, P, I32, P, I32, P, P,
                                       P, I32, I32, P]),
@@ -214,6 +217,18 @@ class ShardContext:
         self._check(lib().oases_profile_end(self.h, ctypes.byref(ms), ctypes.byref(n)),
                     "oases_profile_end")
         return ms.value, n.value
+
+    def profile_timeline(self, cap: int):
+        """End a timing run begun with profile_begin("all", ...): a list of
+        (class name, stream 0 compute / 1 side, start ms, end ms) per timed
+        launch, times relative to the start of the first timed launch."""
+        cls, st = (ctypes.c_int32 * cap)(), (ctypes.c_int32 * cap)()
+        t0, t1 = (ctypes.c_double * cap)(), (ctypes.c_double * cap)()
+        n = ctypes.c_int32(0)
+        self._check(lib().oases_profile_timeline(self.h, cap, cls, st, t0, t1, ctypes.byref(n)),
+                    "oases_profile_timeline")
+        names = {v: k for k, v in KCLASS.items()}
+        return [(names[cls[i]], st[i], t0[i], t1[i]) for i in range(n.value)]
 
     def last_error(self) -> str:
         return lib().oases_last_error(self.h).decode()

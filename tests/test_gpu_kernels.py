@@ -116,7 +116,7 @@ def test_attention_fwd(variant, d, nb, s, nh, causal):
 GEMM_SHAPES = [(200, 192, 128), (1000, 520, 576), (2048, 1024, 1024), (296, 136, 200), (64, 8, 64)]
 
 
-@pytest.mark.parametrize("variant", list(range(20)))
+@pytest.mark.parametrize("variant", list(range(23)))
 @pytest.mark.parametrize("kind", ["fwd", "dx", "dx_gelu", "dx_gelu_tanh", "dw", "dw_colsum"])
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 def test_gemm_layouts_and_tiles(variant, kind, m, n, k):
