@@ -278,6 +278,49 @@ def study_trace(cfg, mode, steps, warmup, timeline_out=None):
             "warmup": warmup, "ms_per_step": t * 1e3, "event_timeline": fig}
 
 
+def study_hbm(reps=10):
+    """What HBM bandwidth a streaming kernel reaches on this GPU, beside the
+    AllReduce-point sum: torch's device copy, the sum kernel with no peers
+    (a copy), and the sum kernel with 3 and 7 peers, all on buffers well
+    beyond the 256 MB Infinity Cache, timed with events over ``reps``
+    back-to-back launches.  GB/s counts the bytes each launch must move."""
+    import torch
+    from tensor_model_transformer_tmp_amd import shard
+
+    dev = torch.device("cuda:0")
+    out = {}
+
+    def timed(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / reps
+        return {"bytes": nbytes, "us": sec * 1e6, "GB/s": nbytes / sec / 1e9}
+
+    n = 1 << 30  # 1 Gi bf16 elements, 2 GiB per buffer
+    a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    out["torch_copy_2GiB"] = timed(lambda: b.copy_(a), 4 * n)
+    out["sum_no_peers_2GiB"] = timed(lambda: shard.allreduce_point(shard.BF16, a, a, 0, b), 4 * n)
+    del a, b
+    # 128 MiB per buffer; then one sub-batch's point of the 8192-hidden pair
+    # (2048 x 8192 bf16 = 32 MiB per buffer, 7 peers)
+    for peers, m, name in ((3, 64 << 20, "sum_3_peers_128MiB_each"), (7, 64 << 20, "sum_7_peers_128MiB_each"),
+                           (7, 2048 * 8192, "sum_7_peers_2048x8192")):
+        own = torch.ones(m, dtype=torch.bfloat16, device=dev)
+        pr = torch.ones(peers, m, dtype=torch.bfloat16, device=dev)
+        y = torch.empty_like(own)
+        out[name] = timed(lambda: shard.allreduce_point(shard.BF16, own, pr, peers, y), (peers + 2) * 2 * m)
+        del own, pr, y
+    torch.cuda.empty_cache()
+    return {"study": "hbm", "reps": reps, "peak_GB/s": HBM_PEAK_GBS, "results": out}
+
+
 def _layer_gemms(cfg, l, T):
     """The six GEMMs of block l over T tokens: (name, a_layout, b_layout, M, N, K)."""
     h, nin, nmid = cfg.hidden, cfg.n_in(l), cfg.n_mid(l)
@@ -362,10 +405,11 @@ def main():
                     help="kernel class for the roofline entry (default: most time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES three times (counter calibration)")
-    ap.add_argument("--study", choices=("ablation", "density", "trace"), default=None,
+    ap.add_argument("--study", choices=("ablation", "density", "trace", "hbm"), default=None,
                     help="run a study instead of the timed step: schedule ablation on --config, "
                          "the batch-split GEMM density study over the bf16 workloads, or "
-                         "--steps eager steps of --schedule alone (for a kernel trace)")
+                         "--steps eager steps of --schedule alone (for a kernel trace), or the "
+                         "streaming-bandwidth reference (copies and sums beyond the Infinity Cache)")
     ap.add_argument("--schedule", default="overlap_streams",
                     choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
                     help="schedule of --study trace")
@@ -386,6 +430,9 @@ def main():
     if args.study == "trace":
         print(json.dumps(study_trace(_preset(args.config), args.schedule, args.steps, args.warmup,
                                      args.timeline_out)), flush=True)
+        return 0
+    if args.study == "hbm":
+        print(json.dumps(study_hbm()), flush=True)
         return 0
     if args.study == "density":
         names = [n for n in gen.PRESET_ORDER if gen.PRESETS[n].dtype == gen.BF16]

@@ -44,7 +44,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 # kernels whose launch count is the class launch count (the other kernels of a
 # multi-kernel class add their time to it)
-_LEAD = {"attn_bwd": "attn_dkdv", "colsum": "colsum_pass1"}
+_LEAD = {"attn_bwd": "attn_dkdv", "colsum": "colsum_pass1", "ln_bwd": "ln_bwd_kernel"}
 
 SOURCES = {
     "gemm_fwd": ("gemm_bf16.hip", "gemm_f32.hip"),
@@ -54,6 +54,9 @@ SOURCES = {
     "attn_bwd": ("attention.hip",),
     "sum": ("elementwise.hip",),
     "colsum": ("elementwise.hip",),
+    "ln_fwd": ("elementwise.hip",),
+    "ln_bwd": ("elementwise.hip",),
+    "dropout_bwd": ("elementwise.hip",),
 }
 
 
@@ -88,7 +91,9 @@ def kernel_class(name: str):
     if m:
         return {("0", "0"): "gemm_fwd", ("0", "1"): "gemm_dx", ("1", "1"): "gemm_dw"}.get(m.groups())
     for key, cls in (("attn_fwd", "attn_fwd"), ("attn_dkdv", "attn_bwd"), ("attn_dq", "attn_bwd"),
-                     ("attn_delta", "attn_bwd"), ("allreduce_", "sum"), ("colsum_pass", "colsum")):
+                     ("attn_delta", "attn_bwd"), ("allreduce_", "sum"), ("colsum_pass", "colsum"),
+                     ("ln_fwd_kernel", "ln_fwd"), ("ln_bwd_kernel", "ln_bwd"), ("ln_grad_pass1", "ln_bwd"),
+                     ("dropout_bwd_kernel", "dropout_bwd")):
         if key in name:
             return cls
     return None
@@ -191,7 +196,7 @@ def _union_len(iv):
 
 
 _LETTER = {"gemm_fwd": "F", "gemm_dx": "X", "gemm_dw": "W", "attn_fwd": "a", "attn_bwd": "b",
-           "sum": "S", "colsum": "c"}
+           "sum": "S", "colsum": "c", "ln_fwd": "n", "ln_bwd": "m", "dropout_bwd": "d"}
 
 
 def timed_trace_rows(path: str, steps: int, warmup: int):
