@@ -239,6 +239,125 @@ __global__ void __launch_bounds__(64 * LN_ROWS)
   }
 }
 
+// The same two kernels for rows of at most 64 * RV vectors, held in
+// registers: RV 16-byte vectors per lane, all of a row's loads in flight
+// before the first add, so the row is read from memory once instead of once
+// per pass with one load per lane in flight.  The arithmetic and its order
+// are those of the kernels above (per lane in ascending vector order, then
+// the wave butterfly), so the results are bit-identical to theirs.
+template <int RV>
+__device__ __forceinline__ void row_stats_reg(const uint4 (&xv)[RV], int hv, int lane, float eps, float &mu,
+                                              float &rstd) {
+  const float inv_h = 1.f / (float)(hv * 8);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < RV; ++i) {
+    if (lane + 64 * i >= hv) break;
+    float f[8];
+    unpack8(xv[i], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += f[e];
+  }
+  mu = wave_sum(sum) * inv_h;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < RV; ++i) {
+    if (lane + 64 * i >= hv) break;
+    float f[8];
+    unpack8(xv[i], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float dlt = f[e] - mu;
+      sq += dlt * dlt;
+    }
+  }
+  rstd = rsqrtf(wave_sum(sq) * inv_h + eps);
+}
+
+template <int RV>
+__device__ __forceinline__ void load_row(const uint4 *r, int hv, int lane, uint4 (&v)[RV]) {
+#pragma unroll
+  for (int i = 0; i < RV; ++i) {
+    const int j = lane + 64 * i;
+    v[i] = j < hv ? r[j] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int RV>
+__global__ void __launch_bounds__(64 * LN_ROWS)
+    ln_fwd_reg_kernel(const uint4 *__restrict__ x, const uint4 *__restrict__ w, const uint4 *__restrict__ b,
+                      uint4 *__restrict__ z, int rows, int hv, float eps) {
+  const int row = blockIdx.x * LN_ROWS + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  uint4 xv[RV];
+  load_row<RV>(x + (int64_t)row * hv, hv, lane, xv);
+  float mu, rstd;
+  row_stats_reg<RV>(xv, hv, lane, eps, mu, rstd);
+#pragma unroll
+  for (int i = 0; i < RV; ++i) {
+    const int j = lane + 64 * i;
+    if (j >= hv) break;
+    float f[8], gw[8], gb[8];
+    unpack8(xv[i], f);
+    unpack8(w[j], gw);
+    unpack8(b[j], gb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf((f[e] - mu) * rstd, gw[e], gb[e]);
+    z[(int64_t)row * hv + j] = make_uint4(cvt_pk(f[0], f[1]), cvt_pk(f[2], f[3]), cvt_pk(f[4], f[5]),
+                                          cvt_pk(f[6], f[7]));
+  }
+}
+
+template <int RV>
+__global__ void __launch_bounds__(64 * LN_ROWS)
+    ln_bwd_reg_kernel(const uint4 *__restrict__ dz, const uint4 *__restrict__ x, const uint4 *__restrict__ w,
+                      const uint4 *__restrict__ g, uint4 *__restrict__ dx, float2 *__restrict__ stats, int rows,
+                      int hv, float eps) {
+  const int row = blockIdx.x * LN_ROWS + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t base = (int64_t)row * hv;
+  uint4 xv[RV], dv[RV];
+  load_row<RV>(x + base, hv, lane, xv);
+  load_row<RV>(dz + base, hv, lane, dv);
+  float mu, rstd;
+  row_stats_reg<RV>(xv, hv, lane, eps, mu, rstd);
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < RV; ++i) {
+    const int j = lane + 64 * i;
+    if (j >= hv) break;
+    float fx[8], fd[8], fw[8];
+    unpack8(xv[i], fx);
+    unpack8(dv[i], fd);
+    unpack8(w[j], fw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gy = fw[e] * fd[e];
+      s1 += gy;
+      s2 += gy * ((fx[e] - mu) * rstd);
+    }
+  }
+  const float inv_h = 1.f / (float)(hv * 8);
+  const float m1 = wave_sum(s1) * inv_h, m2 = wave_sum(s2) * inv_h;
+#pragma unroll
+  for (int i = 0; i < RV; ++i) {
+    const int j = lane + 64 * i;
+    if (j >= hv) break;
+    float fx[8], fd[8], fw[8], fg[8], o[8];
+    unpack8(xv[i], fx);
+    unpack8(dv[i], fd);
+    unpack8(w[j], fw);
+    unpack8(g[base + j], fg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xh = (fx[e] - mu) * rstd;
+      o[e] = fg[e] + rstd * (fw[e] * fd[e] - m1 - xh * m2);
+    }
+    dx[base + j] = make_uint4(cvt_pk(o[0], o[1]), cvt_pk(o[2], o[3]), cvt_pk(o[4], o[5]), cvt_pk(o[6], o[7]));
+  }
+  if (lane == 0) stats[row] = make_float2(mu, rstd);
+}
+
 // dx = g + rstd * (w dz - mean(w dz) - xhat * mean(w dz xhat)); stats[row] = (mean, rstd)
 __global__ void __launch_bounds__(64 * LN_ROWS)
     ln_bwd_kernel(const uint4 *__restrict__ dz, const uint4 *__restrict__ x, const uint4 *__restrict__ w,
@@ -391,9 +510,16 @@ int allreduce_fused_wgs(int64_t nvec) {
 hipError_t layer_norm_fwd(const void *x, const void *w, const void *b, void *z, int rows, int h, float eps,
                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  OASES_LAUNCH(ln_fwd_kernel, dim3((rows + LN_ROWS - 1) / LN_ROWS), dim3(64 * LN_ROWS), s,
-               static_cast<const uint4 *>(x), static_cast<const uint4 *>(w), static_cast<const uint4 *>(b),
-               static_cast<uint4 *>(z), rows, h / 8, eps);
+  const dim3 grid((rows + LN_ROWS - 1) / LN_ROWS), block(64 * LN_ROWS);
+  const uint4 *xp = static_cast<const uint4 *>(x), *wp = static_cast<const uint4 *>(w),
+              *bp = static_cast<const uint4 *>(b);
+  uint4 *zp = static_cast<uint4 *>(z);
+  const int hv = h / 8;
+  // rows held in registers up to 64 x 16 vectors (h = 8192); longer rows in passes
+  if (hv <= 64 * 4) OASES_LAUNCH(ln_fwd_reg_kernel<4>, grid, block, s, xp, wp, bp, zp, rows, hv, eps);
+  else if (hv <= 64 * 8) OASES_LAUNCH(ln_fwd_reg_kernel<8>, grid, block, s, xp, wp, bp, zp, rows, hv, eps);
+  else if (hv <= 64 * 16) OASES_LAUNCH(ln_fwd_reg_kernel<16>, grid, block, s, xp, wp, bp, zp, rows, hv, eps);
+  else OASES_LAUNCH(ln_fwd_kernel, grid, block, s, xp, wp, bp, zp, rows, hv, eps);
   return hipGetLastError();
 }
 
@@ -405,10 +531,22 @@ hipError_t layer_norm_bwd(const void *dz, const void *x, const void *w, const vo
                           float *partial, float *dw, float *db, int rows, int h, float eps, int beta,
                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  OASES_LAUNCH(ln_bwd_kernel, dim3((rows + LN_ROWS - 1) / LN_ROWS), dim3(64 * LN_ROWS), s,
-               static_cast<const uint4 *>(dz), static_cast<const uint4 *>(x), static_cast<const uint4 *>(w),
-               static_cast<const uint4 *>(g), static_cast<uint4 *>(dx), reinterpret_cast<float2 *>(stats), rows,
-               h / 8, eps);
+  {
+    const dim3 grid((rows + LN_ROWS - 1) / LN_ROWS), block(64 * LN_ROWS);
+    const uint4 *dzp = static_cast<const uint4 *>(dz), *xp = static_cast<const uint4 *>(x),
+                *wp = static_cast<const uint4 *>(w), *gp = static_cast<const uint4 *>(g);
+    uint4 *dxp = static_cast<uint4 *>(dx);
+    float2 *st = reinterpret_cast<float2 *>(stats);
+    const int hv = h / 8;
+    if (hv <= 64 * 4)
+      OASES_LAUNCH(ln_bwd_reg_kernel<4>, grid, block, s, dzp, xp, wp, gp, dxp, st, rows, hv, eps);
+    else if (hv <= 64 * 8)
+      OASES_LAUNCH(ln_bwd_reg_kernel<8>, grid, block, s, dzp, xp, wp, gp, dxp, st, rows, hv, eps);
+    else if (hv <= 64 * 16)
+      OASES_LAUNCH(ln_bwd_reg_kernel<16>, grid, block, s, dzp, xp, wp, gp, dxp, st, rows, hv, eps);
+    else
+      OASES_LAUNCH(ln_bwd_kernel, grid, block, s, dzp, xp, wp, gp, dxp, st, rows, hv, eps);
+  }
   const int nchunks = (rows + CS_ROWS - 1) / CS_ROWS;
   float *pw = partial, *pb = partial + (int64_t)nchunks * h;
   OASES_LAUNCH(ln_grad_pass1, dim3((h + 255) / 256, nchunks), dim3(256), s, static_cast<const bf16_t *>(dz),

@@ -35,6 +35,12 @@ def _cfg(**kw):
     return gen.PRESETS["c2_pair_h1024"].with_(**kw)
 
 
+def test_profile_timeline_validation():
+    L = shard.lib()
+    n = ctypes.c_int32(0)
+    assert L.oases_profile_timeline(None, 0, None, None, None, None, ctypes.byref(n)) == shard.E_ARG
+
+
 def test_create_validation():
     for bad, code in ((dict(micro_batch=3), shard.E_SHAPE), (dict(micro_batch=0), shard.E_SHAPE),
                       (dict(hidden=100), shard.E_SHAPE), (dict(head_dim=96), shard.E_SHAPE),

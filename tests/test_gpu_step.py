@@ -45,6 +45,14 @@ FULL = {
     "full_pair_d128_tanh": SMALL["pair_d128"].with_(name="full_pair_d128_tanh", full_block=True,
                                                     drop_q=13107, gelu_tanh=True),
     "full_stack4_nodrop": SMALL["stack4_d64"].with_(name="full_stack4_nodrop", full_block=True, drop_q=0),
+    # LayerNorm rows held in registers at 8 vectors per lane (hidden 3072), and
+    # rows longer than the register form takes (hidden 8256: the multi-pass kernels)
+    "full_ffn_h3072": gen.ShardConfig(name="full_ffn_h3072", blocks=(gen.FFN,), micro_batch=2, seq=24,
+                                      hidden=3072, heads_per_shard=1, head_dim=64, ffn_shard=192,
+                                      tmp_width=2, dtype=gen.BF16, seed=11, full_block=True, drop_q=6554),
+    "full_ffn_h8256": gen.ShardConfig(name="full_ffn_h8256", blocks=(gen.FFN,), micro_batch=2, seq=16,
+                                      hidden=8256, heads_per_shard=1, head_dim=64, ffn_shard=128,
+                                      tmp_width=2, dtype=gen.BF16, seed=12, full_block=True, drop_q=6554),
 }
 
 
@@ -174,3 +182,36 @@ def test_full_block_step_matches_oracle(name, zero_peers):
     dev.ctx.sync()
     _bitwise_equal(dev.results(), got)
     dev.close()
+
+
+def test_event_timeline_of_overlapped_steps():
+    """oases_profile_timeline over two eager sub-batch-stream steps: one entry
+    per kernel-class launch of the op list, on both streams, each ending after
+    it starts; the step's result is the same as without the events."""
+    cfg = SMALL["pair_d128"]
+    dev = DeviceShard(gen.make_inputs(cfg), device="cuda", modes=("overlap_streams",))
+    try:
+        dev.ctx.schedule_step("overlap_streams", False)
+        torch.cuda.synchronize()
+        y0 = dev.y.clone()
+        dev.ctx.profile_begin("all", 1024)
+        for _ in range(2):
+            dev.ctx.schedule_step("overlap_streams", False)
+        rows = dev.ctx.profile_timeline(1024)
+        per_step = len(rows) // 2
+        assert len(rows) == 2 * per_step and per_step > 0
+        kinds = {r[0] for r in rows}
+        assert {"gemm_fwd", "gemm_dx", "gemm_dw", "attn_fwd", "attn_bwd", "sum"} <= kinds
+        assert {r[1] for r in rows} == {0, 1}
+        assert all(b >= a >= 0.0 for _, _, a, b in rows)
+        # C(F) and C(B) of each layer and sub-batch, two steps
+        assert sum(1 for r in rows if r[0] == "sum") == 2 * 4 * cfg.n_layers
+        assert torch.equal(dev.y, y0)
+        # a second run with too small a buffer is an argument error and keeps the run open
+        dev.ctx.profile_begin("all", 1024)
+        dev.ctx.schedule_step("overlap_streams", False)
+        with pytest.raises(Exception):
+            dev.ctx.profile_timeline(1)
+        assert len(dev.ctx.profile_timeline(1024)) == per_step
+    finally:
+        dev.close()
