@@ -278,17 +278,35 @@ def study_trace(cfg, mode, steps, warmup, timeline_out=None):
             "warmup": warmup, "ms_per_step": t * 1e3, "event_timeline": fig}
 
 
-def study_hbm(reps=10):
-    """What HBM bandwidth a streaming kernel reaches on this GPU, beside the
-    AllReduce-point sum: torch's device copy, the sum kernel with no peers
-    (a copy), and the sum kernel with 3 and 7 peers, all on buffers well
-    beyond the 256 MB Infinity Cache, timed with events over ``reps``
-    back-to-back launches.  GB/s counts the bytes each launch must move."""
+def study_peaks(reps=10):
+    """The two rooflines measured on this GPU.  MFMA: a probe kernel of
+    back-to-back independent bf16 32x32x16 MFMAs with register operands, at
+    1, 2 and 4 workgroups of 4 waves per CU.  HBM: torch's device copy, the
+    sum kernel with no peers (a copy), and the sum kernel with 3 and 7 peers,
+    on buffers well beyond the 256 MB Infinity Cache.  Each is timed with
+    events over ``reps`` back-to-back launches; GB/s counts the bytes each
+    launch must move."""
     import torch
     from tensor_model_transformer_tmp_amd import shard
 
     dev = torch.device("cuda:0")
     out = {}
+    mfma = {}
+    for per_cu in (1, 2, 4):
+        wgs = 256 * per_cu
+        buf = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+        iters = 20000 // per_cu
+        flop = shard.mfma_probe(wgs, iters, buf)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            shard.mfma_probe(wgs, iters, buf)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / reps
+        mfma[f"{per_cu}_workgroups_per_cu"] = {"flop": flop, "us": sec * 1e6, "TFLOP/s": flop / sec / 1e12}
+        del buf
 
     def timed(fn, nbytes):
         fn()
@@ -318,7 +336,8 @@ def study_hbm(reps=10):
         out[name] = timed(lambda: shard.allreduce_point(shard.BF16, own, pr, peers, y), (peers + 2) * 2 * m)
         del own, pr, y
     torch.cuda.empty_cache()
-    return {"study": "hbm", "reps": reps, "peak_GB/s": HBM_PEAK_GBS, "results": out}
+    return {"study": "peaks", "reps": reps, "mfma_bf16_peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS, "mfma_probe": mfma,
+            "hbm_peak_GB/s": HBM_PEAK_GBS, "hbm": out}
 
 
 def _layer_gemms(cfg, l, T):
@@ -405,11 +424,12 @@ def main():
                     help="kernel class for the roofline entry (default: most time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES three times (counter calibration)")
-    ap.add_argument("--study", choices=("ablation", "density", "trace", "hbm"), default=None,
+    ap.add_argument("--study", choices=("ablation", "density", "trace", "peaks"), default=None,
                     help="run a study instead of the timed step: schedule ablation on --config, "
                          "the batch-split GEMM density study over the bf16 workloads, or "
                          "--steps eager steps of --schedule alone (for a kernel trace), or the "
-                         "streaming-bandwidth reference (copies and sums beyond the Infinity Cache)")
+                         "measured MFMA and HBM rooflines (MFMA probe; copies and sums beyond the "
+                         "Infinity Cache)")
     ap.add_argument("--schedule", default="overlap_streams",
                     choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
                     help="schedule of --study trace")
@@ -431,8 +451,8 @@ def main():
         print(json.dumps(study_trace(_preset(args.config), args.schedule, args.steps, args.warmup,
                                      args.timeline_out)), flush=True)
         return 0
-    if args.study == "hbm":
-        print(json.dumps(study_hbm()), flush=True)
+    if args.study == "peaks":
+        print(json.dumps(study_peaks()), flush=True)
         return 0
     if args.study == "density":
         names = [n for n in gen.PRESET_ORDER if gen.PRESETS[n].dtype == gen.BF16]

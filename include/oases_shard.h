@@ -244,6 +244,14 @@ int oases_profile_timeline(oases_ctx *c, int32_t cap, int32_t *classes, int32_t 
  * They run one kernel family on `stream` (NULL = default) with the same
  * device code as the step, so each kernel can be checked and timed alone. */
 
+/* Dense bf16 matrix-core throughput probe (a measurement aid, not a step of
+ * the path): `workgroups` workgroups of 4 waves, each wave issuing
+ * 4 * iters independent v_mfma_f32_32x32x16_bf16 (32*32*16*2 FLOP each) on
+ * register operands.  out: caller device buffer of workgroups * 256 floats
+ * (16-byte aligned), overwritten with per-lane checksums.  1 <= workgroups
+ * <= 65536 and iters >= 1, else OASES_E_ARG.  Asynchronous on `stream`. */
+int oases_mfma_probe(int32_t workgroups, int32_t iters, float *out, void *stream);
+
 /* AllReduce-point sum (Section IV): out[i] = own[i] + sum_k peers[k*peer_stride + i]
  * for i < n, float32 accumulation in that order, one rounding to dtype.
  * n_peers >= 0; n a multiple of 8. */

@@ -156,8 +156,8 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-__global__ void __launch_bounds__(256)
-    colsum_pass2(const float *__restrict__ partial, int nchunks, int cols, float *__restrict__ db, int beta) {
+__device__ __forceinline__ void colsum_pass2_body(const float *__restrict__ partial, int nchunks, int cols,
+                                                  float *__restrict__ db, int beta) {
   __shared__ float sm[8][33];
   const int cl = threadIdx.x & 31, ch = threadIdx.x >> 5;
   const int c = blockIdx.x * 32 + cl;
@@ -173,6 +173,20 @@ __global__ void __launch_bounds__(256)
     for (int l = 1; l < 8; ++l) u += sm[l][cl];
     db[c] = r + u;
   }
+}
+
+__global__ void __launch_bounds__(256)
+    colsum_pass2(const float *__restrict__ partial, int nchunks, int cols, float *__restrict__ db, int beta) {
+  colsum_pass2_body(partial, nchunks, cols, db, beta);
+}
+
+// the two column sums of the LayerNorm weight gradients in one launch:
+// blockIdx.y = 0 sums partial_w into dw, 1 sums partial_b into db
+__global__ void __launch_bounds__(256)
+    colsum_pass2_pair(const float *__restrict__ pw, const float *__restrict__ pb, int nchunks, int cols,
+                      float *__restrict__ dw, float *__restrict__ db, int beta) {
+  if (blockIdx.y == 0) colsum_pass2_body(pw, nchunks, cols, dw, beta);
+  else colsum_pass2_body(pb, nchunks, cols, db, beta);
 }
 
 // ---------------------------------------------------------------------------
@@ -551,8 +565,7 @@ hipError_t layer_norm_bwd(const void *dz, const void *x, const void *w, const vo
   float *pw = partial, *pb = partial + (int64_t)nchunks * h;
   OASES_LAUNCH(ln_grad_pass1, dim3((h + 255) / 256, nchunks), dim3(256), s, static_cast<const bf16_t *>(dz),
                static_cast<const bf16_t *>(x), reinterpret_cast<const float2 *>(stats), rows, h, pw, pb);
-  OASES_LAUNCH(colsum_pass2, dim3((h + 31) / 32), dim3(256), s, pw, nchunks, h, dw, beta);
-  OASES_LAUNCH(colsum_pass2, dim3((h + 31) / 32), dim3(256), s, pb, nchunks, h, db, beta);
+  OASES_LAUNCH(colsum_pass2_pair, dim3((h + 31) / 32, 2), dim3(256), s, pw, pb, nchunks, h, dw, db, beta);
   return hipGetLastError();
 }
 

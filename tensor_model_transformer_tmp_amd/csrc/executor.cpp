@@ -833,6 +833,13 @@ int oases_profile_timeline(oases_ctx *c, int32_t cap, int32_t *classes, int32_t 
 
 // ---- single-kernel entry points ----
 
+int oases_mfma_probe(int32_t workgroups, int32_t iters, float *out, void *stream) {
+  if (workgroups < 1 || workgroups > 1 << 16 || iters < 1 || !out) return OASES_E_ARG;
+  if (!aligned16(out)) return OASES_E_ALIGN;
+  return mfma_probe(workgroups, iters, out, static_cast<hipStream_t>(stream)) == hipSuccess ? OASES_OK
+                                                                                          : OASES_E_HIP;
+}
+
 int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int64_t peer_stride,
                           int32_t n_peers, void *out, int64_t n, void *stream) {
   if (dtype != OASES_F32 && dtype != OASES_BF16) return OASES_E_ARG;

@@ -113,6 +113,9 @@ void gemm_bf16_set_variant(int v);
 // AllReduce point: out = own + sum_k peers[k] (float32 accumulation in order),
 // followed by the full block's dropout + residual tail when `tail` has a
 // residual (bf16 only)
+// dense bf16 MFMA throughput probe: `workgroups` x 4 waves, each issuing
+// 4 * iters v_mfma_f32_32x32x16_bf16; out holds workgroups * 256 floats
+hipError_t mfma_probe(int workgroups, int iters, float *out, hipStream_t s);
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
                            int n_peers, void *out, int64_t n, hipStream_t s,
                            const DropRes *tail = nullptr);

@@ -44,7 +44,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 # kernels whose launch count is the class launch count (the other kernels of a
 # multi-kernel class add their time to it)
-_LEAD = {"attn_bwd": "attn_dkdv", "colsum": "colsum_pass1", "ln_bwd": "ln_bwd_kernel"}
+_LEAD = {"attn_bwd": "attn_dkdv", "colsum": "colsum_pass1", "ln_bwd": "ln_bwd"}
 
 SOURCES = {
     "gemm_fwd": ("gemm_bf16.hip", "gemm_f32.hip"),
@@ -92,7 +92,7 @@ def kernel_class(name: str):
         return {("0", "0"): "gemm_fwd", ("0", "1"): "gemm_dx", ("1", "1"): "gemm_dw"}.get(m.groups())
     for key, cls in (("attn_fwd", "attn_fwd"), ("attn_dkdv", "attn_bwd"), ("attn_dq", "attn_bwd"),
                      ("attn_delta", "attn_bwd"), ("allreduce_", "sum"), ("colsum_pass", "colsum"),
-                     ("ln_fwd_kernel", "ln_fwd"), ("ln_bwd_kernel", "ln_bwd"), ("ln_grad_pass1", "ln_bwd"),
+                     ("ln_fwd", "ln_fwd"), ("ln_bwd", "ln_bwd"), ("ln_grad_pass1", "ln_bwd"),
                      ("dropout_bwd_kernel", "dropout_bwd")):
         if key in name:
             return cls

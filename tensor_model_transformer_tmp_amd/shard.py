@@ -28,7 +28,7 @@ KCLASS = {"gemm_fwd": 0, "gemm_dx": 1, "gemm_dw": 2, "attn_fwd": 3, "attn_bwd": 
 EXPORTED = ("oases_create", "oases_workspace_bytes", "oases_bind", "oases_set_streams",
             "layer_fwd", "layer_bwd_recompute", "schedule_step", "oases_schedule_ops",
             "oases_sync", "oases_last_error", "oases_destroy", "oases_profile_begin",
-            "oases_profile_end", "oases_profile_timeline", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
+            "oases_profile_end", "oases_profile_timeline", "oases_mfma_probe", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
             "oases_attention_variant", "oases_sum_grid_cap", "oases_attention_fwd")
 
 
@@ -84,6 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "oases_profile_timeline": (ctypes.c_int, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
                                                   ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
+        "oases_mfma_probe": (ctypes.c_int, [I32, I32, P, P]),
         "oases_allreduce_point": (ctypes.c_int, [I32, P, P, I64, I32, P, I64, P]),
         "oases_gemm": (ctypes.c_int, [I32, I32, I32, I32, I32, I32, I32, P, I32, P, I32, P, I32, P, P,
                                       P, I32, I32, P]),
@@ -250,6 +251,14 @@ class ShardContext:
 def _check_free(r, what):
     if r != OK:
         raise OasesError(r, what)
+
+
+def mfma_probe(workgroups: int, iters: int, out, stream=None):
+    """Dense bf16 MFMA throughput probe; out: float32 device tensor of
+    workgroups * 256 elements.  Returns the FLOPs the launch issues."""
+    _check_free(lib().oases_mfma_probe(workgroups, iters, _ptr(out), _stream_handle(stream)),
+                "oases_mfma_probe")
+    return workgroups * 4 * 4 * iters * 32 * 32 * 16 * 2
 
 
 def allreduce_point(dtype, own, peers, n_peers, out, stream=None):

@@ -35,6 +35,13 @@ def _cfg(**kw):
     return gen.PRESETS["c2_pair_h1024"].with_(**kw)
 
 
+def test_mfma_probe_validation():
+    L = shard.lib()
+    assert L.oases_mfma_probe(0, 1, None, None) == shard.E_ARG
+    assert L.oases_mfma_probe(1, 0, None, None) == shard.E_ARG
+    assert L.oases_mfma_probe(1, 1, None, None) == shard.E_ARG
+
+
 def test_profile_timeline_validation():
     L = shard.lib()
     n = ctypes.c_int32(0)

@@ -168,3 +168,14 @@ def test_gemm_layouts_and_tiles(variant, kind, m, n, k):
                          f"column sums {m}x{n}x{k} variant {variant}")
     finally:
         shard.set_gemm_tile_variant(0)
+
+
+def test_mfma_probe_runs():
+    """The MFMA throughput probe issues its MFMAs (finite, nonzero per-lane
+    checksums) and reports the FLOPs of its launch."""
+    out = torch.zeros(2 * 256, dtype=torch.float32, device="cuda")
+    flop = shard.mfma_probe(2, 3, out)
+    torch.cuda.synchronize()
+    v = out.cpu().numpy()
+    assert flop == 2 * 4 * 4 * 3 * 32 * 32 * 16 * 2
+    assert np.isfinite(v).all() and (v != 0).any()
