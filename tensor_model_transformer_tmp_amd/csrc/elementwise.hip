@@ -542,8 +542,7 @@ int64_t layer_norm_partial_floats(int rows, int h) {
 }
 
 hipError_t layer_norm_bwd(const void *dz, const void *x, const void *w, const void *g, void *dx, float *stats,
-                          float *partial, float *dw, float *db, int rows, int h, float eps, int beta,
-                          hipStream_t s) {
+                          float *partial, int rows, int h, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   {
     const dim3 grid((rows + LN_ROWS - 1) / LN_ROWS), block(64 * LN_ROWS);
@@ -565,6 +564,14 @@ hipError_t layer_norm_bwd(const void *dz, const void *x, const void *w, const vo
   float *pw = partial, *pb = partial + (int64_t)nchunks * h;
   OASES_LAUNCH(ln_grad_pass1, dim3((h + 255) / 256, nchunks), dim3(256), s, static_cast<const bf16_t *>(dz),
                static_cast<const bf16_t *>(x), reinterpret_cast<const float2 *>(stats), rows, h, pw, pb);
+  return hipGetLastError();
+}
+
+hipError_t layer_norm_wgrad(const float *partial, float *dw, float *db, int rows, int h, int beta,
+                            hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int nchunks = (rows + CS_ROWS - 1) / CS_ROWS;
+  const float *pw = partial, *pb = partial + (int64_t)nchunks * h;
   OASES_LAUNCH(colsum_pass2_pair, dim3((h + 31) / 32, 2), dim3(256), s, pw, pb, nchunks, h, dw, db, beta);
   return hipGetLastError();
 }

@@ -209,7 +209,10 @@ struct oases_ctx {
   hipStream_t cs = nullptr, ss = nullptr;
   bool streams_set = false;
   std::vector<hipEvent_t> evF, evCF, evBdX, evCB;
-  std::vector<hipEvent_t> evSB;  // OVERLAP_STREAMS: B_dW(l, 0) done [l < L], fork [L], join [L+1]
+  // OVERLAP_STREAMS: sub-batch 0's dW_in and db_in of layer l done [l], its
+  // LayerNorm weight gradients done [L + l], fork [2L], join [2L + 1], its
+  // dW_out of layer l done [2L + 2 + l]
+  std::vector<hipEvent_t> evSB;
   hipGraphExec_t gexec[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   std::vector<uint8_t> fwd_done, bwd_done;
   std::string err;
@@ -469,19 +472,21 @@ struct Exec {
                       DropRes{}, false))
         return r;
       const oases_layer_params &p = c->prm[l];
-      // the sub-batches' LayerNorm weight gradients accumulate in a fixed order
-      if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(s, c->evSB[d.L + l], 0));
+      float *part = reinterpret_cast<float *>(ws() + W.lnpart[sb]);
       HIPX(layer_norm_bwd(ws() + W.dZ[sb], layer_in(l, sb), p.ln_w, grad_out(l, sb), grad_in(l, sb),
-                          reinterpret_cast<float *>(ws() + W.lnst[sb]), reinterpret_cast<float *>(ws() + W.lnpart[sb]),
-                          static_cast<float *>(p.dln_w), static_cast<float *>(p.dln_b), d.T, d.h, d.eps, sb, s));
+                          reinterpret_cast<float *>(ws() + W.lnst[sb]), part, d.T, d.h, d.eps, s));
+      // the sub-batches' LayerNorm weight gradients accumulate in a fixed
+      // order; with a stream per sub-batch only this last launch waits
+      if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(s, c->evSB[d.L + l], 0));
+      HIPX(layer_norm_wgrad(part, static_cast<float *>(p.dln_w), static_cast<float *>(p.dln_b), d.T, d.h, sb, s));
+      if (by_sb && sb == 0) HIPX(hipEventRecord(c->evSB[d.L + l], s));
     }
     if (overlap) HIPX(hipEventRecord(c->evCB[l * 2 + sb], s));
-    if (by_sb && sb == 0) HIPX(hipEventRecord(c->evSB[d.L + l], s));
     return OASES_OK;
   }
   int op_BdW(int l, int sb) {
-    // the two sub-batches' weight gradients accumulate in a fixed order
-    if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(c->ss, c->evSB[l], 0));
+    // the two sub-batches' weight gradients accumulate in a fixed order, one
+    // GEMM at a time (see weight_grads)
     if (int r = weight_grads(l, sb)) return r;
     if (by_sb && sb == 0) HIPX(hipEventRecord(c->evSB[l], c->cs));
     return OASES_OK;
@@ -498,7 +503,14 @@ struct Exec {
     g.A = dy; g.lda = d.h;
     g.B = d.blocks[l] == OASES_FFN ? sl + W.s_H : sl + W.s_O; g.ldb = nmid;
     g.C = p.dw_out; g.ldc = nmid; g.beta = sb;
+    // with a stream per sub-batch, sub-batch 1 adds into each weight gradient
+    // once sub-batch 0 has written it: its dW_out GEMM waits for sub-batch 0's
+    // dW_out only, and so runs beside sub-batch 0's dW_in GEMM
+    const int L = d.L;
+    if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(c->ss, c->evSB[2 * L + 2 + l], 0));
     if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g, cst(sb))) return r;
+    if (by_sb && sb == 0) HIPX(hipEventRecord(c->evSB[2 * L + 2 + l], c->cs));
+    if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(c->ss, c->evSB[l], 0));  // dW_in and db_in
     GemmArgs g2{};  // dW_in[nin, h] (+)= dpre^T X
     g2.M = nin; g2.N = d.h; g2.K = d.T;
     g2.A = dpre; g2.lda = nin; g2.B = gemm_in(l, sb); g2.ldb = d.h;
@@ -543,7 +555,7 @@ int Exec::gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmA
 int ensure_events(oases_ctx *c) {
   if (!c->evF.empty()) return OASES_OK;
   const int n = c->D.L * 2;
-  c->evSB.resize(n + 2, nullptr);
+  c->evSB.resize(n + 2 + c->D.L, nullptr);
   for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB, &c->evSB}) {
     if (v != &c->evSB) v->resize(n, nullptr);
     // device-internal ordering only: no timing, no system-scope fence

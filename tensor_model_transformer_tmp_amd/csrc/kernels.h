@@ -124,12 +124,15 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
 // z = LayerNorm(x) * w + b per row of x [rows, h] (biased variance, eps)
 hipError_t layer_norm_fwd(const void *x, const void *w, const void *b, void *z, int rows, int h, float eps,
                           hipStream_t s);
-// dx = g + LayerNorm backward of dz at x (weight w); dw (+)= sum_rows dz * xhat,
-// db (+)= sum_rows dz (beta: accumulate).  stats: 2*rows floats; partial:
-// layer_norm_partial_floats(rows, h) floats.
+// dx = g + LayerNorm backward of dz at x (weight w), and the column partials
+// of sum_rows dz * xhat and sum_rows dz (fixed row chunks).  stats: 2*rows
+// floats; partial: layer_norm_partial_floats(rows, h) floats.
 hipError_t layer_norm_bwd(const void *dz, const void *x, const void *w, const void *g, void *dx,
-                          float *stats, float *partial, float *dw, float *db, int rows, int h, float eps,
-                          int beta, hipStream_t s);
+                          float *stats, float *partial, int rows, int h, float eps, hipStream_t s);
+// the LayerNorm weight gradients from those partials, in chunk order:
+// dw (+)= sum_rows dz * xhat, db (+)= sum_rows dz (beta: accumulate)
+hipError_t layer_norm_wgrad(const float *partial, float *dw, float *db, int rows, int h, int beta,
+                            hipStream_t s);
 int64_t layer_norm_partial_floats(int rows, int h);
 // out = dropout backward of g (the mask and scale of `t`), n elements
 hipError_t dropout_bwd(const void *g, void *out, int64_t n, const DropRes &t, hipStream_t s);
