@@ -340,6 +340,47 @@ def study_peaks(reps=10):
             "hbm_peak_GB/s": HBM_PEAK_GBS, "hbm": out}
 
 
+def _gemm_graph_us(shard, torch, M, N, K, reps=20):
+    """Average time of one forward-layout GEMM (automatic tiles) over a
+    hipGraph of ``reps`` back-to-back launches."""
+    dev = torch.device("cuda:0")
+    a = torch.randn(M * K, device=dev).to(torch.bfloat16).view(M, K)
+    b = torch.randn(N * K, device=dev).to(torch.bfloat16).view(N, K)
+    c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    s = torch.cuda.Stream(device=dev)
+    launch = lambda: shard.gemm(shard.BF16, a, b, c, 0, 0, "store", stream=s)
+    with torch.cuda.stream(s):
+        launch()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(reps):
+            launch()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def study_kloop():
+    """Fixed and per-k cost of a 1024-hidden sub-batch GEMM: 2048 x 1024 x k
+    for k = 64 .. 4096, and one 64 x 64 x 64 workgroup, as hipGraph replays;
+    the slope over the long-k end is the k loop's incremental rate."""
+    import torch
+    from tensor_model_transformer_tmp_amd import shard
+    ks = (64, 128, 256, 512, 1024, 2048, 4096)
+    us = {k: _gemm_graph_us(shard, torch, 2048, 1024, k) for k in ks}
+    slope = (us[4096] - us[1024]) / (4096 - 1024)  # us per unit of k
+    return {"study": "kloop", "m": 2048, "n": 1024, "us": {str(k): v for k, v in us.items()},
+            "one_workgroup_64x64x64_us": _gemm_graph_us(shard, torch, 64, 64, 64),
+            "ns_per_k": slope * 1e3, "incremental_tflops": 2 * 2048 * 1024 / (slope * 1e-6) / 1e12}
+
+
 def _layer_gemms(cfg, l, T):
     """The six GEMMs of block l over T tokens: (name, a_layout, b_layout, M, N, K)."""
     h, nin, nmid = cfg.hidden, cfg.n_in(l), cfg.n_mid(l)
@@ -424,12 +465,12 @@ def main():
                     help="kernel class for the roofline entry (default: most time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES three times (counter calibration)")
-    ap.add_argument("--study", choices=("ablation", "density", "trace", "peaks"), default=None,
+    ap.add_argument("--study", choices=("ablation", "density", "trace", "peaks", "kloop"), default=None,
                     help="run a study instead of the timed step: schedule ablation on --config, "
                          "the batch-split GEMM density study over the bf16 workloads, or "
                          "--steps eager steps of --schedule alone (for a kernel trace), or the "
                          "measured MFMA and HBM rooflines (MFMA probe; copies and sums beyond the "
-                         "Infinity Cache)")
+                         "Infinity Cache), or the fixed and per-k cost of a 1024-hidden GEMM")
     ap.add_argument("--schedule", default="overlap_streams",
                     choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
                     help="schedule of --study trace")
@@ -450,6 +491,9 @@ def main():
     if args.study == "trace":
         print(json.dumps(study_trace(_preset(args.config), args.schedule, args.steps, args.warmup,
                                      args.timeline_out)), flush=True)
+        return 0
+    if args.study == "kloop":
+        print(json.dumps(study_kloop()), flush=True)
         return 0
     if args.study == "peaks":
         print(json.dumps(study_peaks()), flush=True)
