@@ -281,7 +281,9 @@ def study_trace(cfg, mode, steps, warmup, timeline_out=None):
 def study_peaks(reps=10):
     """The two rooflines measured on this GPU.  MFMA: a probe kernel of
     back-to-back independent bf16 32x32x16 MFMAs with register operands, at
-    1, 2 and 4 workgroups of 4 waves per CU.  HBM: torch's device copy, the
+    1, 2 and 4 workgroups of 4 waves per CU.  Operand feed: the rate at which
+    a CU takes in L2-resident data by the GEMM loaders' LDS DMA, by loads into
+    registers, and by loads plus LDS writes.  HBM: torch's device copy, the
     sum kernel with no peers (a copy), and the sum kernel with 3 and 7 peers,
     on buffers well beyond the 256 MB Infinity Cache.  Each is timed with
     events over ``reps`` back-to-back launches; GB/s counts the bytes each
@@ -307,6 +309,24 @@ def study_peaks(reps=10):
         sec = e0.elapsed_time(e1) / 1e3 / reps
         mfma[f"{per_cu}_workgroups_per_cu"] = {"flop": flop, "us": sec * 1e6, "TFLOP/s": flop / sec / 1e12}
         del buf
+
+    # operand feed per CU from an L2-resident 4 MB source (1024 workgroups)
+    feed = {}
+    src = torch.ones(4 << 20, dtype=torch.uint8, device=dev)
+    fout = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+    for mode, name in ((0, "lds_dma"), (1, "loads_to_vgprs"), (2, "loads_plus_lds_writes")):
+        nbytes = shard.feed_probe(mode, 1024, 2000, src, fout)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            shard.feed_probe(mode, 1024, 2000, src, fout)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / reps
+        feed[name] = {"bytes": nbytes, "us": sec * 1e6, "TB/s": nbytes / sec / 1e12,
+                      "GB/s_per_CU": nbytes / sec / 1e9 / 256}
+    del src, fout
 
     def timed(fn, nbytes):
         fn()
@@ -337,6 +357,7 @@ def study_peaks(reps=10):
         del own, pr, y
     torch.cuda.empty_cache()
     return {"study": "peaks", "reps": reps, "mfma_bf16_peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS, "mfma_probe": mfma,
+            "operand_feed_probe": feed,
             "hbm_peak_GB/s": HBM_PEAK_GBS, "hbm": out}
 
 

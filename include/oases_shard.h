@@ -252,6 +252,16 @@ int oases_profile_timeline(oases_ctx *c, int32_t cap, int32_t *classes, int32_t 
  * <= 65536 and iters >= 1, else OASES_E_ARG.  Asynchronous on `stream`. */
 int oases_mfma_probe(int32_t workgroups, int32_t iters, float *out, void *stream);
 
+/* Operand feed probe (a measurement aid): `workgroups` workgroups of 4 waves,
+ * each moving 8 * iters 1 KB units from its own 64 KB slice of src, by the
+ * LDS DMA the GEMM loaders use (mode 0), by global loads into registers
+ * (mode 1) or by global loads plus LDS writes (mode 2).  src: device buffer of
+ * src_bytes (a positive multiple of 65536, 16-byte aligned) that the caller
+ * keeps cache-resident by its size; out: workgroups * 256 uint32 checksums.
+ * Bad arguments: OASES_E_ARG.  Asynchronous on `stream`. */
+int oases_feed_probe(int32_t mode, int32_t workgroups, int32_t iters, const void *src, int64_t src_bytes,
+                     uint32_t *out, void *stream);
+
 /* AllReduce-point sum (Section IV): out[i] = own[i] + sum_k peers[k*peer_stride + i]
  * for i < n, float32 accumulation in that order, one rounding to dtype.
  * n_peers >= 0; n a multiple of 8. */

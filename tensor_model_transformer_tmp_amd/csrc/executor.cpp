@@ -852,6 +852,17 @@ int oases_mfma_probe(int32_t workgroups, int32_t iters, float *out, void *stream
                                                                                           : OASES_E_HIP;
 }
 
+int oases_feed_probe(int32_t mode, int32_t workgroups, int32_t iters, const void *src, int64_t src_bytes,
+                     uint32_t *out, void *stream) {
+  if (mode < 0 || mode > 2 || workgroups < 1 || workgroups > 1 << 16 || iters < 1 || !src || !out ||
+      src_bytes < 65536 || src_bytes % 65536)
+    return OASES_E_ARG;
+  if (!aligned16(src) || !aligned16(out)) return OASES_E_ALIGN;
+  return feed_probe(mode, workgroups, iters, src, src_bytes, out, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? OASES_OK
+             : OASES_E_HIP;
+}
+
 int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int64_t peer_stride,
                           int32_t n_peers, void *out, int64_t n, void *stream) {
   if (dtype != OASES_F32 && dtype != OASES_BF16) return OASES_E_ARG;

@@ -116,6 +116,11 @@ void gemm_bf16_set_variant(int v);
 // dense bf16 MFMA throughput probe: `workgroups` x 4 waves, each issuing
 // 4 * iters v_mfma_f32_32x32x16_bf16; out holds workgroups * 256 floats
 hipError_t mfma_probe(int workgroups, int iters, float *out, hipStream_t s);
+// operand feed probe (mode 0 LDS DMA, 1 loads into VGPRs, 2 loads + LDS
+// writes): `workgroups` x 4 waves, each moving 8 * iters 1 KB units from its
+// 64 KB slice of src (src_bytes a multiple of 65536); out: workgroups * 256
+hipError_t feed_probe(int mode, int workgroups, int iters, const void *src, int64_t src_bytes, uint32_t *out,
+                      hipStream_t s);
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
                            int n_peers, void *out, int64_t n, hipStream_t s,
                            const DropRes *tail = nullptr);

@@ -28,7 +28,7 @@ KCLASS = {"gemm_fwd": 0, "gemm_dx": 1, "gemm_dw": 2, "attn_fwd": 3, "attn_bwd": 
 EXPORTED = ("oases_create", "oases_workspace_bytes", "oases_bind", "oases_set_streams",
             "layer_fwd", "layer_bwd_recompute", "schedule_step", "oases_schedule_ops",
             "oases_sync", "oases_last_error", "oases_destroy", "oases_profile_begin",
-            "oases_profile_end", "oases_profile_timeline", "oases_mfma_probe", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
+            "oases_profile_end", "oases_profile_timeline", "oases_mfma_probe", "oases_feed_probe", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
             "oases_attention_variant", "oases_sum_grid_cap", "oases_attention_fwd")
 
 
@@ -85,6 +85,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                   ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
         "oases_mfma_probe": (ctypes.c_int, [I32, I32, P, P]),
+        "oases_feed_probe": (ctypes.c_int, [I32, I32, I32, P, I64, P, P]),
         "oases_allreduce_point": (ctypes.c_int, [I32, P, P, I64, I32, P, I64, P]),
         "oases_gemm": (ctypes.c_int, [I32, I32, I32, I32, I32, I32, I32, P, I32, P, I32, P, I32, P, P,
                                       P, I32, I32, P]),
@@ -259,6 +260,15 @@ def mfma_probe(workgroups: int, iters: int, out, stream=None):
     _check_free(lib().oases_mfma_probe(workgroups, iters, _ptr(out), _stream_handle(stream)),
                 "oases_mfma_probe")
     return workgroups * 4 * 4 * iters * 32 * 32 * 16 * 2
+
+
+def feed_probe(mode: int, workgroups: int, iters: int, src, out, stream=None):
+    """Operand feed probe (0 LDS DMA, 1 loads to registers, 2 loads + LDS
+    writes); src: device tensor of a multiple of 64 KB; out: workgroups * 256
+    32-bit elements.  Returns the bytes the launch moves."""
+    _check_free(lib().oases_feed_probe(mode, workgroups, iters, _ptr(src), src.numel() * src.element_size(),
+                                       _ptr(out), _stream_handle(stream)), "oases_feed_probe")
+    return workgroups * 4 * 8 * iters * 1024
 
 
 def allreduce_point(dtype, own, peers, n_peers, out, stream=None):

@@ -179,3 +179,35 @@ def test_mfma_probe_runs():
     v = out.cpu().numpy()
     assert flop == 2 * 4 * 4 * 3 * 32 * 32 * 16 * 2
     assert np.isfinite(v).all() and (v != 0).any()
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_feed_probe_runs(mode):
+    """The operand feed probe moves the bytes it claims through each path:
+    its per-lane checksums equal the XOR of the source words it read (mode 1)
+    or of the LDS vector it left behind (modes 0 and 2), computed on the host."""
+    iters = 3
+    host = (np.arange(1 << 16) % 251).astype(np.uint8)
+    src = torch.from_numpy(host).to("cuda")
+    out = torch.zeros(2 * 256, dtype=torch.int32, device="cuda")
+    nbytes = shard.feed_probe(mode, 2, iters, src, out)
+    torch.cuda.synchronize()
+    assert nbytes == 2 * 4 * 8 * iters * 1024
+    words = host.view(np.uint32)           # 4-byte words of the 64 KB slice (both workgroups read it)
+    want = np.zeros(256, np.uint32)
+    for t in range(256):
+        lane, wave = t % 64, t // 64
+        if mode == 1:
+            acc = np.zeros(4, np.uint32)
+            for i in range(iters):
+                for u in range(8):
+                    unit = ((i * 8 + u) * 4 + wave) % 64
+                    o = (unit * 1024 + lane * 16) // 4
+                    acc ^= words[o:o + 4]
+        else:                               # the LDS holds the slice itself after the walk
+            o = t * 16 // 4
+            acc = words[o:o + 4]
+        want[t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3]
+    got = out.cpu().numpy().view(np.uint32)
+    np.testing.assert_array_equal(got[:256], want)
+    np.testing.assert_array_equal(got[256:], want)
