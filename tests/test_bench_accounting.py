@@ -10,10 +10,10 @@ import gen
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# counted GFLOP per step (forward / recompute / backward) as tabulated, to
-# three significant figures, in the hot-path scope table written before the
-# code: 2MNK per executed GEMM (the recompute skips the dead row-parallel
-# GEMM) and the causal lower triangle for attention
+# counted GFLOP per step (forward / recompute / backward), worked out by hand
+# from the workload sizes to three significant figures: 2MNK per executed
+# GEMM (the recompute skips the dead row-parallel GEMM) and the causal lower
+# triangle for attention
 EXPECTED_GFLOP = {
     "c2_pair_h1024": (26.9, 16.1, 53.7),
     "c3_pair_h4096": (210, 125, 421),
