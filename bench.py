@@ -4,14 +4,17 @@ A step is one pass of the whole hot path over one micro-batch of seeded
 synthetic input: forward of every block for both sub-batches with the
 AllReduce-point sums overlapping the other sub-batch's compute, then the
 fine-grained recompute and backward of every block (Oases overlapped
-schedule).  The overlap is realised with a side stream and events, by running
-each sum on extra workgroups of the next GEMM launch, or with one stream per
-sub-batch; each eagerly or as one hipGraph.  The fastest of the six is timed.
+schedule).  By default the overlap is realised with one stream per
+sub-batch (each sub-batch's compute and AllReduce points on its own stream,
+so one sub-batch's sums run beside the other's compute), issued eagerly.
 
 Prints one JSON line.  ``value`` is the counted (algorithmic) TFLOP/s of the
-step; the roofline entry is for the kernel class with the most time per
-step, timed with HIP events carried in its kernels' dispatch packets; the
-CPU baseline is the float64 oracle on this host's cores.
+step at the median per-step time (HIP events on the compute stream).  Every
+kernel-class launch of the timed steps carries a HIP event pair in its own
+dispatch packets: the per-class durations, the roofline entry (the class
+with the most time per step) and the fraction of the AllReduce-point sums'
+time that ran beside compute kernels all come from those steps.  The CPU
+baseline is the float64 oracle on this host's cores.
 """
 from __future__ import annotations
 
@@ -29,7 +32,7 @@ import gen  # noqa: E402
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 vector
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "c2_pair_h1024"
+DEFAULT_WORKLOAD = "c5_pair_h8192"
 METRIC = "TMP-shard fwd+recompute+bwd TFLOP/s per GPU; % MFMA peak; % reduction hidden"
 
 
@@ -239,16 +242,6 @@ def event_timeline(dev, mode, steps):
     return fig, text
 
 
-def _plain_ms(dev, mode, steps):
-    import torch
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        dev.ctx.schedule_step(mode, False)
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3
-
-
 def study_trace(cfg, mode, steps, warmup, timeline_out=None):
     """Steps of one schedule only, issued eagerly, for a kernel trace: warm-up
     and timed steps are all the library runs, so a rocprofv3 kernel trace of
@@ -281,9 +274,7 @@ def study_trace(cfg, mode, steps, warmup, timeline_out=None):
 def study_peaks(reps=10):
     """The two rooflines measured on this GPU.  MFMA: a probe kernel of
     back-to-back independent bf16 32x32x16 MFMAs with register operands, at
-    1, 2 and 4 workgroups of 4 waves per CU.  Operand feed: the rate at which
-    a CU takes in L2-resident data by the GEMM loaders' LDS DMA, by loads into
-    registers, and by loads plus LDS writes.  HBM: torch's device copy, the
+    1, 2 and 4 workgroups of 4 waves per CU.  HBM: torch's device copy, the
     sum kernel with no peers (a copy), and the sum kernel with 3 and 7 peers,
     on buffers well beyond the 256 MB Infinity Cache.  Each is timed with
     events over ``reps`` back-to-back launches; GB/s counts the bytes each
@@ -309,24 +300,6 @@ def study_peaks(reps=10):
         sec = e0.elapsed_time(e1) / 1e3 / reps
         mfma[f"{per_cu}_workgroups_per_cu"] = {"flop": flop, "us": sec * 1e6, "TFLOP/s": flop / sec / 1e12}
         del buf
-
-    # operand feed per CU from an L2-resident 4 MB source (1024 workgroups)
-    feed = {}
-    src = torch.ones(4 << 20, dtype=torch.uint8, device=dev)
-    fout = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
-    for mode, name in ((0, "lds_dma"), (1, "loads_to_vgprs"), (2, "loads_plus_lds_writes")):
-        nbytes = shard.feed_probe(mode, 1024, 2000, src, fout)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            shard.feed_probe(mode, 1024, 2000, src, fout)
-        e1.record()
-        torch.cuda.synchronize()
-        sec = e0.elapsed_time(e1) / 1e3 / reps
-        feed[name] = {"bytes": nbytes, "us": sec * 1e6, "TB/s": nbytes / sec / 1e12,
-                      "GB/s_per_CU": nbytes / sec / 1e9 / 256}
-    del src, fout
 
     def timed(fn, nbytes):
         fn()
@@ -357,7 +330,6 @@ def study_peaks(reps=10):
         del own, pr, y
     torch.cuda.empty_cache()
     return {"study": "peaks", "reps": reps, "mfma_bf16_peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS, "mfma_probe": mfma,
-            "operand_feed_probe": feed,
             "hbm_peak_GB/s": HBM_PEAK_GBS, "hbm": out}
 
 
@@ -494,7 +466,10 @@ def main():
                          "Infinity Cache), or the fixed and per-k cost of a 1024-hidden GEMM")
     ap.add_argument("--schedule", default="overlap_streams",
                     choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
-                    help="schedule of --study trace")
+                    help="schedule of the timed steps and of --study trace (default: one stream per "
+                         "sub-batch, the fastest realisation of the overlapped schedule)")
+    ap.add_argument("--issue", default="eager", choices=("eager", "graph"),
+                    help="issue the timed steps eagerly or as hipGraph replays")
     ap.add_argument("--timeline-out", default=None, metavar="PATH",
                     help="--study trace: write the event timeline's text chart here")
     args = ap.parse_args()
@@ -526,86 +501,96 @@ def main():
 
     import torch
     from tensor_model_transformer_tmp_amd.device import DeviceShard
+    from tensor_model_transformer_tmp_amd.rocprof_summary import overlap_report
 
     cfg = _preset(args.config)
     inp = gen.make_inputs(cfg)
-    dev = DeviceShard(inp, device="cuda:0", modes=("overlap_fine", "overlap_fused", "overlap_streams",
-                                                    "serial_fine"))
+    mode = args.schedule
+    dev = DeviceShard(inp, device="cuda:0", modes=(mode, "serial_fine"))
     del inp
+    use_graph = args.issue == "graph"
+    cs = dev.compute
 
-    def run(mode, graph, n):
-        for _ in range(n):
-            dev.ctx.schedule_step(mode, graph)
-
-    def timed(mode, graph, steps, warmup):
-        run(mode, graph, warmup)
+    def steps_with_events(n, graph):
+        """n steps, each bracketed by HIP events on the compute stream (the
+        step forks the side stream from it and joins it back), with a
+        synchronize on both sides of the whole run: (wall s, [ms per step])."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run(mode, graph, steps)
+        ev[0].record(cs)
+        for i in range(n):
+            dev.ctx.schedule_step(mode, graph)
+            ev[i + 1].record(cs)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        wall = time.perf_counter() - t0
+        return wall, [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
 
-    # The overlapped fine-grained schedule has three realisations: the sums on
-    # a side stream ordered with events (overlap_fine), the sums as extra
-    # workgroups of the next GEMM launch on the compute stream
-    # (overlap_fused), or one stream per sub-batch carrying its compute and
-    # its sums (overlap_streams).  Each is issued eagerly or replayed as one
-    # hipGraph; all six are probed briefly and the fastest is the timed
-    # region.  The same kernels serialised on one stream give the reference
-    # for the hidden-reduction estimate.
-    probe = max(3, args.steps // 5)
-    launch = {(m, g): timed(m, g, probe, 2) for m in ("overlap_fine", "overlap_fused", "overlap_streams")
-              for g in (False, True)}
-    mode, use_graph = min(launch, key=launch.get)
-    sec = timed(mode, use_graph, args.steps, args.warmup)
-    sec_serial = timed("serial_fine", use_graph, max(5, args.steps // 2), 3)
+    def median(v):
+        v = sorted(v)
+        return 0.5 * (v[(len(v) - 1) // 2] + v[len(v) // 2])
 
-    # Per-kernel-class timing: eager overlapped steps with a pair of HIP events
-    # recorded on the kernel's own launch stream around every launch of the class.
-    def class_time(kclass, steps):
-        dev.ctx.profile_begin(kclass, 16384)
-        run("overlap_fine", False, steps)
-        ms, n = dev.ctx.profile_end()
-        return ms / 1e3, n
+    for _ in range(args.warmup):
+        dev.ctx.schedule_step(mode, use_graph)
+    torch.cuda.synchronize()
 
-    # how much of the sums' time ran beside compute kernels, from one event
-    # timeline of the timed schedule (eager; a fused sum has no launch of its own)
-    # The events cost time per launch; where they slow the step by more than
-    # 15% (small workloads, many short launches) the timeline no longer shows
-    # the uninstrumented overlap and its figure is not reported.
-    tl_mode = "overlap_streams" if mode == "overlap_fused" else mode
-    tl_fig, _ = event_timeline(dev, tl_mode, 5)
-    tl_fig["schedule"] = tl_mode + "+eager"
-    tl_fig["ms_per_step_plain"] = _plain_ms(dev, tl_mode, 5)
-    tl_fig["instrumented_over_plain"] = tl_fig["ms_per_step_with_events"] / tl_fig["ms_per_step_plain"]
-    beside = tl_fig["hidden_frac"] if tl_fig["instrumented_over_plain"] <= 1.15 else None
+    # The timed region.  Issued eagerly, every kernel-class launch also
+    # carries a HIP event pair in its own dispatch packets (on the stream it
+    # is launched on), so the per-class durations and the overlap timeline
+    # come from exactly the steps that are timed.  A hipGraph replay cannot
+    # carry them: then the same number of eager steps is instrumented after it.
+    cap = min(1 << 16, sum(class_launches(cfg, kc) for kc in KERNEL_CLASSES) * args.steps + 64)
+    if not use_graph:
+        dev.ctx.profile_begin("all", cap)
+    wall, per_step = steps_with_events(args.steps, use_graph)
+    if use_graph:
+        dev.ctx.profile_begin("all", cap)
+        steps_with_events(args.steps, False)
+    tl = dev.ctx.profile_timeline(cap)
+    # the same schedule without instrumentation, for its cost
+    _, plain = steps_with_events(max(5, args.steps // 2), use_graph)
+    # each kernel class alone: a few steps of the serial schedule (same
+    # kernels, one stream, nothing running beside a launch), events as above
+    n_solo = 5
+    dev.ctx.profile_begin("all", cap)
+    steps_with_events(n_solo, False)
+    tl_solo = dev.ctx.profile_timeline(cap)
+    dev.close()
 
-    prof_steps = max(3, min(args.steps, 20))
+    # (start ns, end ns, stream, class, name)
+    rows = [(a * 1e6, b * 1e6, ("compute", "side", "other")[st], cls, cls) for cls, st, a, b in tl]
+    solo = {}
+    for cls, _, a, b in tl_solo:
+        solo.setdefault(cls, []).append((b - a) * 1e3)  # us
+    fig, _ = overlap_report(rows, args.steps)
+    ms_step = median(per_step)
+    f, r, b = step_flops(cfg)
+    flops = f + r + b
+    value = flops / (ms_step / 1e3) / 1e12
+
+    n_steps = args.steps
     kernels = {}
     for kc in KERNEL_CLASSES:
         work, unit = class_work(cfg, kc)
-        if work == 0:
+        durs = [(b_ - a_) / 1e3 for a_, b_, _, c_, _ in rows if c_ == kc]  # us
+        if work == 0 or not durs:
             continue
-        t, n = class_time(kc, prof_steps)
-        per_step = n // prof_steps
-        assert per_step == class_launches(cfg, kc), (kc, n, prof_steps)
-        avg = t / n
+        per_step_n = len(durs) // n_steps
+        assert per_step_n == class_launches(cfg, kc), (kc, len(durs), n_steps)
+        avg = sum(durs) / len(durs) / 1e6  # s
+        solo_avg = sum(solo[kc]) / len(solo[kc]) / 1e6
         if unit == "FLOP":
-            ach, pk, u = work / per_step / avg / 1e12, (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == gen.BF16
-                                                        else FP32_PEAK_TFLOPS), "TFLOP/s"
+            pk, scale, u = (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == gen.BF16 else FP32_PEAK_TFLOPS), 1e12, "TFLOP/s"
         else:
-            ach, pk, u = work / per_step / avg / 1e9, HBM_PEAK_GBS, "GB/s"
-        kernels[kc] = {"launches_per_step": per_step, "avg_us": avg * 1e6,
-                       "us_per_step": t / prof_steps * 1e6, "achieved": ach, "unit": u,
-                       "frac": ach / pk, "work_per_launch": work / per_step,
-                       "work_unit": unit}
-    dev.close()
+            pk, scale, u = HBM_PEAK_GBS, 1e9, "GB/s"
+        wpl = work / per_step_n
+        kernels[kc] = {"launches_per_step": per_step_n, "avg_us": avg * 1e6,
+                       "median_us": median(durs), "us_per_step": sum(durs) / n_steps,
+                       "achieved": wpl / avg / scale, "unit": u, "frac": wpl / avg / scale / pk,
+                       "work_per_launch": wpl, "work_unit": unit,
+                       "solo_avg_us": solo_avg * 1e6, "solo_achieved": wpl / solo_avg / scale,
+                       "solo_frac": wpl / solo_avg / scale / pk}
 
-    f, r, b = step_flops(cfg)
-    flops = f + r + b
-    value = flops / sec / 1e12
-    sum_per_step = kernels["sum"]["us_per_step"] / 1e6
-    hidden = (sec_serial - sec) / sum_per_step if sum_per_step > 0 else None
     k = args.roofline_kernel or max(kernels, key=lambda c: kernels[c]["us_per_step"])
     kk = kernels[k]
     hbm = kk["unit"] == "GB/s"
@@ -613,13 +598,18 @@ def main():
             "peak": HBM_PEAK_GBS if hbm else (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == gen.BF16
                                               else FP32_PEAK_TFLOPS),
             "unit": kk["unit"], "frac": kk["frac"], "traffic": stored_traffic(k, cfg.name),
-            "kernel": f"{k}: {kk['launches_per_step'] * prof_steps} launches over {prof_steps} "
-                      f"eager overlapped steps, avg {kk['avg_us']:.2f} us, "
-                      f"{kk['work_per_launch']:.4g} {kk['work_unit']} per launch"}
+            "kernel": f"{k}: {kk['launches_per_step'] * n_steps} launches in the {n_steps} timed "
+                      f"steps ({mode}, eager, events in the dispatch packets), avg {kk['avg_us']:.2f} us, "
+                      f"{kk['work_per_launch']:.4g} {kk['work_unit']} per launch",
+            # the same class alone (serial schedule, after the timed steps): in
+            # the timed steps a launch shares the GPU with the other sub-batch's
+            # kernels, so its duration is longer than the kernel's own
+            "solo": {"achieved": kk["solo_achieved"], "frac": kk["solo_frac"], "avg_us": kk["solo_avg_us"],
+                     "launches": kk["launches_per_step"] * n_solo}}
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == gen.BF16 else "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "blocks": ["attn" if x == gen.ATTN else "ffn"
@@ -631,13 +621,14 @@ def main():
                    "parallelism": "one TMP shard, 1 GPU",
                    **({"full_block": True, "dropout_p": cfg.drop_q / 65536.0, "gelu_tanh": cfg.gelu_tanh}
                       if cfg.full_block else {})},
-        "mfma_peak_frac": value / MFMA_BF16_PEAK_TFLOPS,
-        "reduction_hidden_frac": hidden,
-        "reduction_beside_compute_frac": beside,
-        "event_timeline": tl_fig,
-        "serial_ms_per_step": sec_serial * 1e3,
-        "launch_probe_ms": {f"{m}+{'graph' if g else 'eager'}": t * 1e3 for (m, g), t in launch.items()},
-        "sum_ms_per_step": sum_per_step * 1e3,
+        "timing": "median of per-step HIP-event times on the compute stream over the timed steps",
+        "wall_ms_per_step": wall / args.steps * 1e3,
+        "plain_ms_per_step": median(plain),
+        "mfma_peak_frac": value / (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == gen.BF16 else FP32_PEAK_TFLOPS),
+        # the part of the AllReduce-point sums' time during which a GEMM or
+        # attention kernel of either stream was running, over the timed steps
+        "reduction_hidden_frac": fig["hidden_frac"],
+        "overlap": fig,
         "kernels": kernels,
         "gflop_per_step": {"fwd": f / 1e9, "recompute": r / 1e9, "bwd": b / 1e9},
         "roofline": roof,

@@ -183,23 +183,39 @@ int oases_bind(oases_ctx *c, const oases_buffers *b, const oases_layer_params *p
 int oases_set_streams(oases_ctx *c, void *compute_stream, void *side_stream);
 
 /* Forward operator of block `layer` for sub-batch `sub_batch` (0 or 1):
- * F on the compute stream (waiting for the C(F) that produced its input),
- * then StartAsync of C(F) on the side stream.  Requires layer_fwd of
- * (layer-1, sub_batch) earlier in the step.  Intermediates are not kept. */
+ * the computation operator F_i followed by StartAsync of its communication
+ * operator C_i(F) (Section IV: the forward sequence (F_i, C_i(F), F_j) and the
+ * executor's StartAsync / Sync of Algorithm 1).  F runs on the compute stream
+ * (after a Sync on the C(F) that produced its input), then C(F) -- the sum of
+ * the shard's partial output and the w-1 peer partials -- on the side stream.
+ * Requires layer_fwd of (layer-1, sub_batch) earlier in the step.  Only the
+ * block input is kept (checkpoint); intermediates are not.
+ * Errors (nothing is enqueued): OASES_E_ARG for layer / sub_batch out of
+ * range, OASES_E_STATE if called out of order, before oases_bind /
+ * oases_set_streams, or twice in one step; OASES_E_HIP if a launch fails. */
 int layer_fwd(oases_ctx *c, int32_t layer, int32_t sub_batch);
 
-/* Fine-grained backward of block `layer`, sub-batch `sub_batch`: R (recompute
- * from the stored input, no row GEMM, no C(R)), then B_dX after a Sync on the
- * C(B) of (layer+1, sub_batch), StartAsync of C(B) on the side stream, then
- * B_dW on the compute stream.  Requires layer_fwd of the top layer for this
- * sub-batch and layer_bwd_recompute of (layer+1, sub_batch); sub-batch 1 of a
- * layer requires sub-batch 0 of the same layer first (gradient accumulation
- * order).  Otherwise OASES_E_STATE. */
+/* Fine-grained backward of block `layer`, sub-batch `sub_batch` (Section IV,
+ * Fig. 4d and Eq. (1)): R (recompute from the stored input, started after
+ * the forward's communication operator, so no row GEMM and no C(R): by
+ * Eq. (1) the AllReduce inputs' gradient is dY itself), then B_dX after a
+ * Sync on the C(B) of (layer+1, sub_batch), StartAsync of C(B) on the side
+ * stream, then B_dW on the compute stream.  Requires layer_fwd of the top
+ * layer for this sub-batch and layer_bwd_recompute of (layer+1, sub_batch);
+ * sub-batch 1 of a layer requires sub-batch 0 of the same layer first
+ * (gradient accumulation order).  Errors as layer_fwd (OASES_E_STATE for
+ * these orderings). */
 int layer_bwd_recompute(oases_ctx *c, int32_t layer, int32_t sub_batch);
 
 /* One whole step (forward + backward of every layer and both sub-batches) in
- * `mode`.  use_graph != 0 captures the step into a hipGraph on its first
- * call per mode and replays it afterwards. */
+ * `mode` (Section IV, Algorithm 1: split the batch into two sub-batches, run
+ * the forward with each sub-batch's AllReduce points overlapping the other's
+ * compute, then the backward in fine-grained recompute order).  use_graph != 0
+ * captures the step into a hipGraph on its first call per mode (needs a
+ * non-default compute stream) and replays it afterwards.  Errors: OASES_E_ARG
+ * for a bad mode or a workspace too small for it; OASES_E_STATE before
+ * oases_bind / oases_set_streams; OASES_E_HIP if a launch or the capture
+ * fails.  Nothing is enqueued on a validation error. */
 int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph);
 
 /* Op list of `mode` as issued by schedule_step, four int32 per op:
@@ -251,16 +267,6 @@ int oases_profile_timeline(oases_ctx *c, int32_t cap, int32_t *classes, int32_t 
  * (16-byte aligned), overwritten with per-lane checksums.  1 <= workgroups
  * <= 65536 and iters >= 1, else OASES_E_ARG.  Asynchronous on `stream`. */
 int oases_mfma_probe(int32_t workgroups, int32_t iters, float *out, void *stream);
-
-/* Operand feed probe (a measurement aid): `workgroups` workgroups of 4 waves,
- * each moving 8 * iters 1 KB units from its own 64 KB slice of src, by the
- * LDS DMA the GEMM loaders use (mode 0), by global loads into registers
- * (mode 1) or by global loads plus LDS writes (mode 2).  src: device buffer of
- * src_bytes (a positive multiple of 65536, 16-byte aligned) that the caller
- * keeps cache-resident by its size; out: workgroups * 256 uint32 checksums.
- * Bad arguments: OASES_E_ARG.  Asynchronous on `stream`. */
-int oases_feed_probe(int32_t mode, int32_t workgroups, int32_t iters, const void *src, int64_t src_bytes,
-                     uint32_t *out, void *stream);
 
 /* AllReduce-point sum (Section IV): out[i] = own[i] + sum_k peers[k*peer_stride + i]
  * for i < n, float32 accumulation in that order, one rounding to dtype.
@@ -319,6 +325,29 @@ int oases_attention_variant(int32_t variant);
  * s_pad = s rounded up to a multiple of 64).  bf16 only; d in {64, 128}. */
 int oases_attention_fwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t causal,
                         const void *qkv, void *o, float *lse, void *stream);
+
+/* Attention backward of the attention block (Section IV: the backward B of
+ * the attention operator of an F_i; the softmax probabilities are rebuilt
+ * from lse, nothing of the forward beyond O and lse is kept).  Inputs: QKV
+ * [nb*s, 3a] as in oases_attention_fwd, O and dO [nb*s, a] (bf16), lse
+ * [nb, n_h, s_pad] (float32, as oases_attention_fwd writes it).  Output:
+ * dQKV [nb*s, 3a] (bf16; columns [dQ | dK | dV], head-major), fully written.
+ * workspace: caller-owned device scratch of at least
+ * oases_attention_bwd_workspace_bytes(nb, s, n_h) bytes (delta =
+ * rowsum(dO * O) per query, then the dS matrices [nb*n_h, s_pad, s_pad] in
+ * bf16 that the dK/dV kernel passes to the dQ kernel); it needs no
+ * initialisation and is overwritten.  d in {64, 128}; 16-byte aligned
+ * pointers.  Errors (before any launch; message in oases_last_call_error):
+ * OASES_E_ARG, OASES_E_ALIGN; OASES_E_HIP if a launch fails.  Asynchronous on
+ * `stream`. */
+int oases_attention_bwd_workspace_bytes(int32_t nb, int32_t s, int32_t n_h, size_t *bytes);
+int oases_attention_bwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t causal, const void *qkv,
+                        const void *o, const void *dout, const float *lse, void *dqkv, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Message of the last failing call on this thread that takes no context
+ * (oases_create and the single-kernel entry points); "" if none. */
+const char *oases_last_call_error(void);
 
 #ifdef __cplusplus
 }

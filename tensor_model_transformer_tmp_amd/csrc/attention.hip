@@ -36,11 +36,14 @@
 // units), so an unscaled probability is at most 2^8.  l and O share that
 // reference, so the result is the same softmax; only the rounding differs.
 //
-// Backward (no atomics): the dQ kernel owns queries, computes their
-// delta = rowsum(dO * O) (stored for the next kernel) and walks key blocks
-// (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T); the dK/dV kernel then owns
-// keys and walks query blocks (S = Q K^T, dP = dO V^T, dV^T += dO^T P,
-// dK^T += Q^T dS).  P is rebuilt from lse.
+// Backward (no atomics, five matmuls per block pair): a small kernel forms
+// delta = rowsum(dO * O) per query; the dK/dV kernel then owns keys and walks
+// query blocks (S = Q K^T, dP = dO V^T, P rebuilt from lse, dS = P (dP - delta),
+// dV^T += dO^T P, dK^T += Q^T dS) and stores dS (bf16) in a scratch matrix
+// [nb*n_h, s_pad, s_pad]; the dQ kernel owns queries and walks the key blocks
+// of their causal range, staging K and dS blocks (dQ^T += K^T dS^T).  Every
+// dS entry the dQ kernel reads was written by the dK/dV kernel (the causal
+// lower triangle of 32 x 32 blocks, masked entries as zeros).
 #include <math.h>
 
 #include "common.h"
@@ -135,6 +138,21 @@ struct Blk {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int k = k_lo + r * 8 + hl * 4 + (i >> 2);
+      const bf16_t *p = blk + k * D + (((n >> 3) ^ swz(k)) << 3) + (n & 7);
+      v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(lds_void_t *)p);
+    }
+    const uint2 lo = __builtin_bit_cast(uint2, v[0]), hi = __builtin_bit_cast(uint2, v[1]);
+    return as_frag(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+  // The same in natural row order: rows k_lo + hl*8 + 0..7 (the order of a
+  // row-fragment read of 8 consecutive columns, e.g. of a dS row).
+  __device__ __forceinline__ static bf16x8 frag_tn(const bf16_t *blk, int col, int k_lo, int hl) {
+    const int i = threadIdx.x & 15;
+    const int n = (col - i) + 4 * (i & 3);
+    v4i16 v[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int k = k_lo + hl * 8 + r * 4 + (i >> 2);
       const bf16_t *p = blk + k * D + (((n >> 3) ^ swz(k)) << 3) + (n & 7);
       v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(lds_void_t *)p);
     }
@@ -468,8 +486,8 @@ template <int D, int OWN>
 __global__ void __launch_bounds__(64 * NW)
     attn_dkdv_kernel(const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout,
                      const float *__restrict__ lse, const float *__restrict__ delta,
-                     bf16_t *__restrict__ dqkv, int s, int s_pad, int nh, int causal, float scale_log2,
-                     float scale, int pair) {
+                     bf16_t *__restrict__ dsm, bf16_t *__restrict__ dqkv, int s, int s_pad, int nh,
+                     int causal, float scale_log2, float scale, int pair) {
   using B = Blk<D>;
   using C = DkdvCfg<D, OWN>;
   constexpr int SPLIT = C::SPLIT, DL = C::DL;
@@ -541,7 +559,11 @@ __global__ void __launch_bounds__(64 * NW)
       sc = mfma32(B::frag(qs, l32, kk, hl), kf[kk], sc);   // S[q][key]
       dp = mfma32(B::frag(dos, l32, kk, hl), vf[kk], dp);  // dP[q][key]
     }
-    const bool edge = (causal && qs0 < kw0 + 31) || qs0 + RB > s;
+    // masked: queries past the sequence, keys after the query (causal), and
+    // keys past the sequence (lanes of a partial last key tile compute on a
+    // clamped key; their dS entries are read by the dQ kernel, so they must
+    // be zero)
+    const bool edge = (causal && qs0 < kw0 + 31) || qs0 + RB > s || kw0 + RB > s;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 L4 = *reinterpret_cast<const float4 *>(ls + g * 8 + hl * 4);
@@ -554,12 +576,29 @@ __global__ void __launch_bounds__(64 * NW)
         float ds = p * (dp[r] - dl[e]);
         if (edge) {
           const int q = qs0 + acc_row(r, hl);
-          const bool ok = q < s && (!causal || kj <= q);
+          const bool ok = q < s && kj < s && (!causal || kj <= q);
           p = ok ? p : 0.f;
           ds = ok ? ds : 0.f;
         }
         sc[r] = p;
         dp[r] = ds;
+      }
+    }
+    // dS[q][key] in bf16 for the dQ kernel.  A lane holds one key (column)
+    // and 16 query rows; lanes 2i and 2i+1 (adjacent keys) trade one value
+    // so that each stores two adjacent keys of one row in a 4-byte word: the
+    // even lane row acc_row(r), the odd lane row acc_row(r) + 1.  Waves whose
+    // keys start past the sequence store nothing (columns stay below s_pad).
+    if (kw0 < s) {
+      bf16_t *drow = dsm + ((int64_t)bh * s_pad + qs0) * s_pad + (kj & ~1);
+      const bool odd = lane & 1;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float x = odd ? dp[r] : dp[r + 1];
+        const float y = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+        const uint32_t w = odd ? cvt_pk(y, dp[r + 1]) : cvt_pk(dp[r], y);
+        *reinterpret_cast<uint32_t *>(drow + (int64_t)(acc_row(r, hl) + (odd ? 1 : 0)) * s_pad) = w;
       }
     }
 #pragma unroll
@@ -588,71 +627,108 @@ __global__ void __launch_bounds__(64 * NW)
 }
 
 // ---------------------------------------------------------------------------
-// backward: dQ.  A wave owns 32 queries and walks 32-key blocks of K and V.
+// backward: delta = rowsum(dO * O) per query, float32.  A workgroup covers
+// 256 / (D/8) query rows of one (sequence, head); D/8 lanes read a row's
+// 16-byte chunks and add their products in a fixed butterfly order.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+    attn_delta_kernel(const bf16_t *__restrict__ o, const bf16_t *__restrict__ dout, float *__restrict__ delta,
+                      int s, int s_pad, int nh) {
+  constexpr int CPR = D / 8, ROWS = 256 / CPR;
+  const int bh = blockIdx.y, b = bh / nh, h = bh % nh, a = nh * D;
+  const int c = threadIdx.x % CPR, q = blockIdx.x * ROWS + threadIdx.x / CPR;
+  float part = 0.f;
+  if (q < s) {
+    const int64_t off = (int64_t)(b * s + q) * a + h * D + c * 8;
+    const uint4 x = *reinterpret_cast<const uint4 *>(o + off);
+    const uint4 y = *reinterpret_cast<const uint4 *>(dout + off);
+    part = lo_f32(x.x) * lo_f32(y.x) + hi_f32(x.x) * hi_f32(y.x) + lo_f32(x.y) * lo_f32(y.y) +
+           hi_f32(x.y) * hi_f32(y.y) + lo_f32(x.z) * lo_f32(y.z) + hi_f32(x.z) * hi_f32(y.z) +
+           lo_f32(x.w) * lo_f32(y.w) + hi_f32(x.w) * hi_f32(y.w);
+  }
+#pragma unroll
+  for (int m = 1; m < CPR; m <<= 1) part += __shfl_xor(part, m);
+  if (c == 0 && q < s) delta[(int64_t)bh * s_pad + q] = part;
+}
+
+// ---------------------------------------------------------------------------
+// backward: dQ.  A wave owns 32 queries and walks the 32-key blocks of their
+// causal range, staging K blocks and the matching 32 x 32 dS blocks (written
+// by the dK/dV kernel): dQ^T += K^T dS^T, then dQ = scale * dS K.
 // ---------------------------------------------------------------------------
 template <int D, int OWN>
+struct DqCfg {
+  static constexpr int SPLIT = NW / OWN;
+  static constexpr int KU = SPLIT * Blk<D>::UNITS;  // K units per step
+  static constexpr int SU = OWN * SPLIT * 2;        // dS units per step (two per 32 x 32 block)
+  static_assert((KU + SU) % NW == 0, "units per wave");
+  static constexpr int DL = (KU + SU) / NW;
+  static constexpr int K_BYTES = SPLIT * Blk<D>::BYTES;
+  static constexpr int STAGE_BYTES = K_BYTES + OWN * SPLIT * 2048;
+  static constexpr int STAGES = 3 * STAGE_BYTES <= LDS_BUDGET ? 3 : 2;
+  static constexpr int RED_BYTES = NW * D * 32 * 4;
+  static constexpr int LDS = STAGES * STAGE_BYTES > RED_BYTES ? STAGES * STAGE_BYTES : RED_BYTES;
+};
+
+// chunk swizzle of a staged 32 x 32 dS block (64-byte rows): 16-byte chunk c
+// of row r at c ^ ds_swz(r), so a fragment read of 16 consecutive rows at one
+// chunk touches distinct bank slots
+__device__ __forceinline__ int ds_swz(int r) { return (r >> 2) & 3; }
+
+template <int D, int OWN>
 __global__ void __launch_bounds__(64 * NW)
-    attn_dq_kernel(const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ o, const bf16_t *__restrict__ dout,
-                   const float *__restrict__ lse, float *__restrict__ delta,
-                   bf16_t *__restrict__ dqkv, int s, int s_pad, int nh, int causal, float scale_log2,
-                   float scale, int pair) {
+    attn_dq_kernel(const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dsm, bf16_t *__restrict__ dqkv,
+                   int s, int s_pad, int nh, int causal, float scale, int pair) {
   using B = Blk<D>;
-  using C = KvCfg<D, OWN>;  // same staging as the forward: K and V blocks
+  using C = DqCfg<D, OWN>;
   constexpr int SPLIT = C::SPLIT, DL = C::DL;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int own = wave % OWN, sp = wave / OWN;
   const int ntile = (s + 32 * OWN - 1) / (32 * OWN);
+  const int bh = blockIdx.y, b = bh / nh, h = bh % nh;
+  const int a = nh * D, ld = 3 * a;
+  const bf16_t *Kp = qkv + (int64_t)b * s * ld + a + h * D;
+  const bf16_t *dsb = dsm + (int64_t)bh * s_pad * s_pad;
+
+  // DMA units of a step: unit uu = j*NW + wave; K units first (K block
+  // uu / UNITS of the step), then dS units (block (own o, split p) =
+  // (uu - KU) / 2, rows 16 (uu - KU) % 2 .. +15).  K offsets are relative
+  // to the step's first key row; dS units keep their row in the tile, split
+  // and source chunk.
+  uint32_t koff[DL];
+  int ldso[DL], drow[DL], dsp[DL], dcol[DL];
+#pragma unroll
+  for (int j = 0; j < DL; ++j) {
+    const int uu = j * NW + wave;
+    if (uu < C::KU) {
+      const int g = uu / B::UNITS, u = uu % B::UNITS;
+      int r, cb;
+      B::unit_src(u, lane, r, cb);
+      koff[j] = (uint32_t)((g * RB + r) * ld * 2 + cb);
+      ldso[j] = g * B::BYTES + u * 1024;
+      drow[j] = dsp[j] = dcol[j] = 0;
+    } else {
+      const int du = uu - C::KU, bi = du >> 1, u = du & 1;
+      const int row = u * 16 + (lane >> 2);
+      koff[j] = 0;
+      drow[j] = (bi / SPLIT) * 32 + row;
+      dsp[j] = bi % SPLIT;
+      dcol[j] = ((lane & 3) ^ ds_swz(row)) << 3;
+      ldso[j] = C::K_BYTES + bi * 2048 + u * 1024;
+    }
+  }
+
   // tiles as in the forward: ntile-1-x, and with pairing also x
   for (int rep = 0; rep < 1 + pair; ++rep) {
   const int tile = rep == 0 ? ntile - 1 - (int)blockIdx.x : (int)blockIdx.x;
   if (rep == 1 && tile >= ntile - 1 - (int)blockIdx.x) break;
   if (rep == 1) lds_barrier();  // the previous tile's combine has read the LDS
   const int q0 = tile * 32 * OWN;
-  const int qw0 = q0 + own * 32, qi = qw0 + l32;
-  const int bh = blockIdx.y, b = bh / nh, h = bh % nh;
-  const int a = nh * D, ld = 3 * a;
-  const bf16_t *Qp = qkv + (int64_t)b * s * ld + h * D;
-  const bf16_t *Kp = Qp + a;
-  const bf16_t *dOp = dout + (int64_t)b * s * a + h * D;
+  const int qw0 = q0 + own * 32;
 
-  KvStager<D, OWN> stg;
-  stg.init(wave, lane, ld, a);
-
-  bf16x8 qf[D / 16], df[D / 16];
-  const int qrow = min(qi, s - 1);
-  const bf16_t *Op = o + (int64_t)b * s * a + h * D + (int64_t)qrow * a + hl * 8;
-  uint4 of[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    qf[kk] = load_frag(Qp + (int64_t)qrow * ld + kk * 16 + hl * 8);
-    df[kk] = load_frag(dOp + (int64_t)qrow * a + kk * 16 + hl * 8);
-    of[kk] = *reinterpret_cast<const uint4 *>(Op + kk * 16);
-  }
-  const bool q_ok = qi < s;
-  const float lse2 = q_ok ? lse[(int64_t)bh * s_pad + qi] * LOG2E : 0.f;
-  // delta = rowsum(dO * O) of this lane's query: the lane holds half of the
-  // row's d values (the same half of dO as its dQ fragments), the lane 32
-  // away the other half.  Stored once per query for the dK/dV kernel.
-  float part = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const uint4 x = of[kk], y = __builtin_bit_cast(uint4, df[kk]);
-    part += lo_f32(x.x) * lo_f32(y.x) + hi_f32(x.x) * hi_f32(y.x) + lo_f32(x.y) * lo_f32(y.y) +
-            hi_f32(x.y) * hi_f32(y.y) + lo_f32(x.z) * lo_f32(y.z) + hi_f32(x.z) * hi_f32(y.z) +
-            lo_f32(x.w) * lo_f32(y.w) + hi_f32(x.w) * hi_f32(y.w);
-  }
-  const float dsum = part + other_half(part);
-  const float dlt = q_ok ? dsum : 0.f;
-  if (sp == 0 && hl == 0 && q_ok) delta[(int64_t)bh * s_pad + qi] = dsum;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    settle(qf[kk]);
-    settle(df[kk]);
-  }
-  settle(lse2);
-  settle(dlt);
   f32x16 dq[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) zero(dq[t]);
@@ -662,36 +738,37 @@ __global__ void __launch_bounds__(64 * NW)
   const int nst = (nkb + SPLIT - 1) / SPLIT;
 
   const uint32_t smem_lds = lds_addr(smem);
-  auto issue = [&](int st, int slot) { stg.issue(Kp, ld, s, st * SPLIT * RB, smem_lds + slot * C::STAGE_BYTES); };
+  auto issue = [&](int st, int slot) {
+    const int row0 = st * SPLIT * RB;
+    const uint32_t stage = smem_lds + slot * C::STAGE_BYTES;
+    const bool full = row0 + SPLIT * RB <= s;
+    const bf16_t *kbase = Kp + (int64_t)row0 * ld;
+#pragma unroll
+    for (int j = 0; j < DL; ++j) {
+      if (j * NW + wave < C::KU) {  // uniform across the wave
+        if (full) dma16_s(kbase, koff[j], stage + ldso[j]);
+        else dma_clamped(Kp, ld, row0, s, koff[j], stage + ldso[j]);
+      } else {
+        // rows past the sequence and blocks past the walk read a valid
+        // block; their results are never used
+        const int q = min(q0 + drow[j], s - 1);
+        const int kb = min(st * SPLIT + dsp[j], nkb - 1);
+        dma16_v(dsb + (int64_t)q * s_pad + kb * RB + dcol[j], stage + ldso[j]);
+      }
+    }
+  };
   auto compute = [&](int st, int slot) {
     const int kb = st * SPLIT + sp, k0 = kb * RB;
     if (kb >= nkb || (causal && k0 > qw0 + 31)) return;
-    const bf16_t *ks = reinterpret_cast<const bf16_t *>(smem + slot * C::STAGE_BYTES + sp * 2 * B::BYTES);
-    const bf16_t *vs = ks + B::ELEMS;
-    f32x16 sc, dp;
-    zero(sc);
-    zero(dp);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      sc = mfma32(B::frag(ks, l32, kk, hl), qf[kk], sc);  // S^T[key][q]
-      dp = mfma32(B::frag(vs, l32, kk, hl), df[kk], dp);  // dP^T[key][q]
-    }
-    const bool edge = (causal && k0 + 31 > qw0) || k0 + RB > s || !q_ok;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2_fast(fmaf(sc[r], scale_log2, -lse2));
-      float ds = p * (dp[r] - dlt);
-      if (edge) {
-        const int key = k0 + acc_row(r, hl);
-        ds = (q_ok && key < s && (!causal || key <= qi)) ? ds : 0.f;
-      }
-      dp[r] = ds;
-    }
+    const char *stg = smem + slot * C::STAGE_BYTES;
+    const bf16_t *ks = reinterpret_cast<const bf16_t *>(stg + sp * B::BYTES);
+    const bf16_t *dss = reinterpret_cast<const bf16_t *>(stg + C::K_BYTES + (own * SPLIT + sp) * 2048);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const bf16x8 dsf = acc_to_frag(dp, hh);
+      // dS^T fragment: query l32, keys hh*16 + hl*8 .. +7 (one row chunk)
+      const bf16x8 dsf = load_frag(dss + l32 * RB + (((hh * 2 + hl) ^ ds_swz(l32)) << 3));
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) dq[t] = mfma32(B::frag_t(ks, t * 32 + l32, hh * 16, hl), dsf, dq[t]);
+      for (int t = 0; t < D / 32; ++t) dq[t] = mfma32(B::frag_tn(ks, t * 32 + l32, hh * 16, hl), dsf, dq[t]);
     }
   };
   walk<C::STAGES, DL>(nst, issue, compute);
@@ -753,19 +830,22 @@ hipError_t fwd_launch(int nb, int s, int nh, int causal, int pair, const void *q
   return hipSuccess;
 }
 
-// dQ first (it also computes and stores delta), then dK / dV
+// delta, then dK / dV (which writes dS), then dQ from dS
 template <int D, int OWN>
 hipError_t bwd_launch(int nb, int s, int nh, int causal, int pair, const void *qkv, const void *o,
-                      const void *dout, const float *lse, float *delta, void *dqkv, hipStream_t st) {
+                      const void *dout, const float *lse, float *delta, void *dsm, void *dqkv, hipStream_t st) {
   const float scale = 1.f / sqrtf((float)D);
   const int s_pad = attn_lse_stride(s);
   const bf16_t *q = static_cast<const bf16_t *>(qkv), *d_o = static_cast<const bf16_t *>(dout);
-  bf16_t *dq = static_cast<bf16_t *>(dqkv);
+  bf16_t *dq = static_cast<bf16_t *>(dqkv), *ds = static_cast<bf16_t *>(dsm);
+  constexpr int DROWS = 256 / (D / 8);
+  OASES_LAUNCH((attn_delta_kernel<D>), dim3((s + DROWS - 1) / DROWS, nb * nh), dim3(256), st,
+               static_cast<const bf16_t *>(o), d_o, delta, s, s_pad, nh);
   const dim3 grid(tile_wgs(s, OWN, pair), nb * nh);
-  OASES_LAUNCH((attn_dq_kernel<D, OWN>), grid, dim3(64 * NW), st, q, static_cast<const bf16_t *>(o), d_o, lse,
-               delta, dq, s, s_pad, nh, causal, scale * LOG2E, scale, pair);
-  OASES_LAUNCH((attn_dkdv_kernel<D, OWN>), grid, dim3(64 * NW), st, q, d_o, lse, delta, dq, s, s_pad, nh,
-               causal, scale * LOG2E, scale, pair);
+  OASES_LAUNCH((attn_dkdv_kernel<D, OWN>), grid, dim3(64 * NW), st, q, d_o, lse,
+               static_cast<const float *>(delta), ds, dq, s, s_pad, nh, causal, scale * LOG2E, scale, pair);
+  OASES_LAUNCH((attn_dq_kernel<D, OWN>), grid, dim3(64 * NW), st, q, static_cast<const bf16_t *>(ds), dq, s,
+               s_pad, nh, causal, scale, pair);
   return hipSuccess;
 }
 
@@ -781,12 +861,12 @@ hipError_t fwd_d(int nb, int s, int nh, int causal, const void *qkv, void *o, fl
 
 template <int D>
 hipError_t bwd_d(int nb, int s, int nh, int causal, const void *qkv, const void *o, const void *dout,
-                 const float *lse, float *delta, void *dqkv, hipStream_t st) {
+                 const float *lse, float *delta, void *dsm, void *dqkv, hipStream_t st) {
   const AttnPlan pl = pick_plan(s, nb * nh, causal, true);
   switch (pl.own) {
-    case 4: return bwd_launch<D, 4>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dqkv, st);
-    case 2: return bwd_launch<D, 2>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dqkv, st);
-    default: return bwd_launch<D, 1>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dqkv, st);
+    case 4: return bwd_launch<D, 4>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dsm, dqkv, st);
+    case 2: return bwd_launch<D, 2>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dsm, dqkv, st);
+    default: return bwd_launch<D, 1>(nb, s, nh, causal, pl.pair, qkv, o, dout, lse, delta, dsm, dqkv, st);
   }
 }
 
@@ -804,11 +884,17 @@ hipError_t attention_fwd(int nb, int s, int nh, int d, int causal, const void *q
   return hipErrorInvalidValue;
 }
 
+int64_t attn_ds_elems(int nb, int nh, int s) {
+  const int64_t sp = attn_lse_stride(s);
+  return (int64_t)nb * nh * sp * sp;
+}
+
 hipError_t attention_bwd(int nb, int s, int nh, int d, int causal, const void *qkv, const void *o,
-                         const void *dout, const float *lse, float *delta, void *dqkv, hipStream_t st) {
+                         const void *dout, const float *lse, float *delta, void *dsm, void *dqkv,
+                         hipStream_t st) {
   if (nb <= 0 || s <= 0 || nh <= 0) return hipSuccess;
-  if (d == 64) return bwd_d<64>(nb, s, nh, causal, qkv, o, dout, lse, delta, dqkv, st);
-  if (d == 128) return bwd_d<128>(nb, s, nh, causal, qkv, o, dout, lse, delta, dqkv, st);
+  if (d == 64) return bwd_d<64>(nb, s, nh, causal, qkv, o, dout, lse, delta, dsm, dqkv, st);
+  if (d == 128) return bwd_d<128>(nb, s, nh, causal, qkv, o, dout, lse, delta, dsm, dqkv, st);
   return hipErrorInvalidValue;
 }
 

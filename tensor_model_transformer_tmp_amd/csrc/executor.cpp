@@ -16,7 +16,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cstdio>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -67,6 +66,7 @@ struct Dims {
 // workspace layout for one mode (byte offsets)
 struct WsLayout {
   size_t P[2], dxo[2], dpre[2], dO[2], delta[2];
+  size_t ads[2];  // attention backward: the dS matrices passed from the dK/dV to the dQ kernel
   size_t act_bytes;      // one activation slot
   size_t act0;           // first slot; slot (i, sb) at act0 + (i*2 + sb) * act_bytes
   int n_slots;
@@ -93,6 +93,7 @@ WsLayout make_layout(const Dims &D, int mode) {
     o.dpre[sb] = take((size_t)D.T * D.max_n_in() * D.esz);
     o.dO[sb] = D.any_attn ? take((size_t)D.T * D.a * D.esz) : 0;
     o.delta[sb] = D.any_attn ? take(lse_bytes) : 0;
+    o.ads[sb] = D.any_attn ? take((size_t)attn_ds_elems(D.nb, D.ns, D.s) * 2) : 0;
     o.dS[sb] = D.full ? take(th) : 0;
     o.dZ[sb] = D.full ? take(th) : 0;
     o.lnst[sb] = D.full ? take((size_t)D.T * 2 * sizeof(float)) : 0;
@@ -199,7 +200,56 @@ std::vector<Op> build_ops(int L, int mode) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
+// message of the last failing context-free call on this thread
+thread_local std::string g_call_err;
+
 }  // namespace
+
+namespace oases {
+
+int call_fail(int code, const std::string &msg) {
+  g_call_err = msg;
+  return code;
+}
+
+size_t attention_bwd_scratch_bytes(int nb, int s, int nh) {
+  return align_up((size_t)nb * nh * attn_lse_stride(s) * sizeof(float)) + (size_t)attn_ds_elems(nb, nh, s) * 2;
+}
+
+int attention_bwd_validate(int nb, int s, int nh, int d, int causal, const void *qkv, const void *o,
+                           const void *dout, const float *lse, void *dqkv, size_t *need) {
+  *need = 0;
+  if (nb < 0 || s < 0 || nh < 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1))
+    return call_fail(OASES_E_ARG, "attention backward: need nb, s, n_h >= 0, d in {64, 128}, causal in {0, 1}");
+  if ((int64_t)nb * s * 3 * nh * d > ((int64_t)1 << 31) || s > (1 << 20))
+    return call_fail(OASES_E_ARG, "attention backward: qkv larger than 2^31 elements or s > 2^20");
+  if (nb == 0 || s == 0 || nh == 0) return OASES_OK;
+  if (!qkv || !o || !dout || !lse || !dqkv) return call_fail(OASES_E_ARG, "attention backward: a pointer is NULL");
+  if (!aligned16(qkv) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) || !aligned16(dqkv))
+    return call_fail(OASES_E_ALIGN, "attention backward: a pointer is not 16-byte aligned");
+  *need = attention_bwd_scratch_bytes(nb, s, nh);
+  return OASES_OK;
+}
+
+int attention_bwd_call(int nb, int s, int nh, int d, int causal, const void *qkv, const void *o,
+                       const void *dout, const float *lse, void *dqkv, void *scratch, size_t scratch_bytes,
+                       hipStream_t st) {
+  size_t need = 0;
+  if (int r = attention_bwd_validate(nb, s, nh, d, causal, qkv, o, dout, lse, dqkv, &need)) return r;
+  if (need == 0) return OASES_OK;  // empty problem
+  if (!scratch) return call_fail(OASES_E_ARG, "attention backward: scratch is NULL");
+  if (!aligned16(scratch)) return call_fail(OASES_E_ALIGN, "attention backward: scratch is not 16-byte aligned");
+  if (scratch_bytes < need)
+    return call_fail(OASES_E_ARG, "attention backward: scratch of " + std::to_string(scratch_bytes) +
+                                      " bytes, need " + std::to_string(need));
+  float *delta = static_cast<float *>(scratch);
+  void *dsm = static_cast<char *>(scratch) + align_up((size_t)nb * nh * attn_lse_stride(s) * sizeof(float));
+  const hipError_t e = attention_bwd(nb, s, nh, d, causal, qkv, o, dout, lse, delta, dsm, dqkv, st);
+  if (e != hipSuccess) return call_fail(OASES_E_HIP, std::string("attention backward: ") + hipGetErrorString(e));
+  return OASES_OK;
+}
+
+}  // namespace oases
 
 struct oases_ctx {
   Dims D;
@@ -448,7 +498,7 @@ struct Exec {
       if (int r = prof_begin(KC_ATTN_BWD, cst(sb))) return r;
       HIPX(attention_bwd(d.nb, d.s, d.ns, d.d, d.causal, sl + W.s_QKV, sl + W.s_O, ws() + W.dO[sb],
                          reinterpret_cast<const float *>(sl + W.s_LSE),
-                         reinterpret_cast<float *>(ws() + W.delta[sb]), dpre, cst(sb)));
+                         reinterpret_cast<float *>(ws() + W.delta[sb]), ws() + W.ads[sb], dpre, cst(sb)));
       if (int r = prof_end(KC_ATTN_BWD, cst(sb))) return r;
     }
     GemmArgs g{};  // dX_own = dpre W_in
@@ -611,10 +661,7 @@ int oases_create(const oases_config *cfg, oases_ctx **out) {
   Dims d;
   std::string err;
   const int r = check_config(cfg, &d, &err);
-  if (r) {
-    std::fprintf(stderr, "oases_create: %s\n", err.c_str());
-    return r;
-  }
+  if (r) return call_fail(r, "oases_create: " + err);
   oases_ctx *c = new oases_ctx();
   c->D = std::move(d);
   c->fwd_done.assign(c->D.L * 2, 0);
@@ -852,17 +899,6 @@ int oases_mfma_probe(int32_t workgroups, int32_t iters, float *out, void *stream
                                                                                           : OASES_E_HIP;
 }
 
-int oases_feed_probe(int32_t mode, int32_t workgroups, int32_t iters, const void *src, int64_t src_bytes,
-                     uint32_t *out, void *stream) {
-  if (mode < 0 || mode > 2 || workgroups < 1 || workgroups > 1 << 16 || iters < 1 || !src || !out ||
-      src_bytes < 65536 || src_bytes % 65536)
-    return OASES_E_ARG;
-  if (!aligned16(src) || !aligned16(out)) return OASES_E_ALIGN;
-  return feed_probe(mode, workgroups, iters, src, src_bytes, out, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? OASES_OK
-             : OASES_E_HIP;
-}
-
 int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int64_t peer_stride,
                           int32_t n_peers, void *out, int64_t n, void *stream) {
   if (dtype != OASES_F32 && dtype != OASES_BF16) return OASES_E_ARG;
@@ -942,5 +978,21 @@ int oases_attention_fwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t c
   const hipError_t e = attention_fwd(nb, s, n_h, d, causal, qkv, o, lse, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? OASES_OK : OASES_E_HIP;
 }
+
+int oases_attention_bwd_workspace_bytes(int32_t nb, int32_t s, int32_t n_h, size_t *bytes) {
+  if (!bytes || nb < 0 || s < 0 || n_h < 0 || s > (1 << 20))
+    return call_fail(OASES_E_ARG, "oases_attention_bwd_workspace_bytes: bad argument");
+  *bytes = attention_bwd_scratch_bytes(nb, s, n_h);
+  return OASES_OK;
+}
+
+int oases_attention_bwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t causal, const void *qkv,
+                        const void *o, const void *dout, const float *lse, void *dqkv, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  return attention_bwd_call(nb, s, n_h, d, causal, qkv, o, dout, lse, dqkv, workspace, workspace_bytes,
+                            static_cast<hipStream_t>(stream));
+}
+
+const char *oases_last_call_error(void) { return g_call_err.c_str(); }
 
 }  // extern "C"

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace oases {
 
 // Kernel timing.  While a pair of events is armed (the executor arms one pair
@@ -116,11 +118,6 @@ void gemm_bf16_set_variant(int v);
 // dense bf16 MFMA throughput probe: `workgroups` x 4 waves, each issuing
 // 4 * iters v_mfma_f32_32x32x16_bf16; out holds workgroups * 256 floats
 hipError_t mfma_probe(int workgroups, int iters, float *out, hipStream_t s);
-// operand feed probe (mode 0 LDS DMA, 1 loads into VGPRs, 2 loads + LDS
-// writes): `workgroups` x 4 waves, each moving 8 * iters 1 KB units from its
-// 64 KB slice of src (src_bytes a multiple of 65536); out: workgroups * 256
-hipError_t feed_probe(int mode, int workgroups, int iters, const void *src, int64_t src_bytes, uint32_t *out,
-                      hipStream_t s);
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
                            int n_peers, void *out, int64_t n, hipStream_t s,
                            const DropRes *tail = nullptr);
@@ -162,10 +159,28 @@ void attention_set_variant(int v);
 // O [nb*s, a], lse [nb, nh, attn_lse_stride(s)] (natural log).  bf16, d in {64, 128}.
 hipError_t attention_fwd(int nb, int s, int nh, int d, int causal, const void *qkv, void *o,
                          float *lse, hipStream_t st);
-// Backward: delta[nb, nh, attn_lse_stride(s)] = rowsum(dO * O) workspace;
-// writes dQKV [nb*s, 3a].
+// Backward: writes dQKV [nb*s, 3a].  Scratch: delta [nb, nh, attn_lse_stride(s)]
+// floats (rowsum(dO * O)) and dsm, attn_ds_elems(nb, nh, s) bf16 (the dS
+// matrices [nb*nh, s_pad, s_pad] passed from the dK/dV to the dQ kernel).
+int64_t attn_ds_elems(int nb, int nh, int s);
 hipError_t attention_bwd(int nb, int s, int nh, int d, int causal, const void *qkv,
                          const void *o, const void *dout, const float *lse, float *delta,
-                         void *dqkv, hipStream_t st);
+                         void *dsm, void *dqkv, hipStream_t st);
+
+// ---- host-side entry helpers (executor.cpp) ----
+// record the message of a failing context-free call (oases_last_call_error);
+// returns code
+int call_fail(int code, const std::string &msg);
+// scratch of the attention backward: delta, then the dS matrices (256-byte aligned)
+size_t attention_bwd_scratch_bytes(int nb, int s, int nh);
+// argument checks of the attention backward (no HIP call); *need = scratch
+// bytes, 0 for an empty problem
+int attention_bwd_validate(int nb, int s, int nh, int d, int causal, const void *qkv, const void *o,
+                           const void *dout, const float *lse, void *dqkv, size_t *need);
+// validated attention backward on caller scratch; an oases_status, with the
+// message of a failure kept for oases_last_call_error()
+int attention_bwd_call(int nb, int s, int nh, int d, int causal, const void *qkv, const void *o,
+                       const void *dout, const float *lse, void *dqkv, void *scratch, size_t scratch_bytes,
+                       hipStream_t st);
 
 }  // namespace oases

@@ -28,8 +28,9 @@ KCLASS = {"gemm_fwd": 0, "gemm_dx": 1, "gemm_dw": 2, "attn_fwd": 3, "attn_bwd": 
 EXPORTED = ("oases_create", "oases_workspace_bytes", "oases_bind", "oases_set_streams",
             "layer_fwd", "layer_bwd_recompute", "schedule_step", "oases_schedule_ops",
             "oases_sync", "oases_last_error", "oases_destroy", "oases_profile_begin",
-            "oases_profile_end", "oases_profile_timeline", "oases_mfma_probe", "oases_feed_probe", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
-            "oases_attention_variant", "oases_sum_grid_cap", "oases_attention_fwd")
+            "oases_profile_end", "oases_profile_timeline", "oases_mfma_probe", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
+            "oases_attention_variant", "oases_sum_grid_cap", "oases_attention_fwd",
+            "oases_attention_bwd_workspace_bytes", "oases_attention_bwd", "oases_last_call_error")
 
 
 class OasesError(RuntimeError):
@@ -85,7 +86,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                   ctypes.POINTER(ctypes.c_double),
                                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
         "oases_mfma_probe": (ctypes.c_int, [I32, I32, P, P]),
-        "oases_feed_probe": (ctypes.c_int, [I32, I32, I32, P, I64, P, P]),
         "oases_allreduce_point": (ctypes.c_int, [I32, P, P, I64, I32, P, I64, P]),
         "oases_gemm": (ctypes.c_int, [I32, I32, I32, I32, I32, I32, I32, P, I32, P, I32, P, I32, P, P,
                                       P, I32, I32, P]),
@@ -93,6 +93,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "oases_attention_variant": (ctypes.c_int, [I32]),
         "oases_sum_grid_cap": (ctypes.c_int, [I32]),
         "oases_attention_fwd": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P]),
+        "oases_attention_bwd_workspace_bytes": (ctypes.c_int, [I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]),
+        "oases_attention_bwd": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "oases_last_call_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -251,7 +254,7 @@ class ShardContext:
 
 def _check_free(r, what):
     if r != OK:
-        raise OasesError(r, what)
+        raise OasesError(r, f"{what}: {lib().oases_last_call_error().decode()}")
 
 
 def mfma_probe(workgroups: int, iters: int, out, stream=None):
@@ -260,15 +263,6 @@ def mfma_probe(workgroups: int, iters: int, out, stream=None):
     _check_free(lib().oases_mfma_probe(workgroups, iters, _ptr(out), _stream_handle(stream)),
                 "oases_mfma_probe")
     return workgroups * 4 * 4 * iters * 32 * 32 * 16 * 2
-
-
-def feed_probe(mode: int, workgroups: int, iters: int, src, out, stream=None):
-    """Operand feed probe (0 LDS DMA, 1 loads to registers, 2 loads + LDS
-    writes); src: device tensor of a multiple of 64 KB; out: workgroups * 256
-    32-bit elements.  Returns the bytes the launch moves."""
-    _check_free(lib().oases_feed_probe(mode, workgroups, iters, _ptr(src), src.numel() * src.element_size(),
-                                       _ptr(out), _stream_handle(stream)), "oases_feed_probe")
-    return workgroups * 4 * 8 * iters * 1024
 
 
 def allreduce_point(dtype, own, peers, n_peers, out, stream=None):
@@ -317,3 +311,19 @@ def set_attention_variant(v: int):
 def attention_fwd(nb, s, nh, d, causal, qkv, o, lse, stream=None):
     _check_free(lib().oases_attention_fwd(nb, s, nh, d, int(causal), _ptr(qkv), _ptr(o), _ptr(lse),
                                           _stream_handle(stream)), "oases_attention_fwd")
+
+
+def attention_bwd_workspace_bytes(nb, s, nh) -> int:
+    out = ctypes.c_size_t(0)
+    _check_free(lib().oases_attention_bwd_workspace_bytes(nb, s, nh, ctypes.byref(out)),
+                "oases_attention_bwd_workspace_bytes")
+    return out.value
+
+
+def attention_bwd(nb, s, nh, d, causal, qkv, o, dout, lse, dqkv, workspace, stream=None):
+    """dQKV of the attention block; workspace: a device tensor of at least
+    attention_bwd_workspace_bytes(nb, s, nh) bytes."""
+    _check_free(lib().oases_attention_bwd(nb, s, nh, d, int(causal), _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse),
+                                          _ptr(dqkv), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream_handle(stream)), "oases_attention_bwd")

@@ -42,15 +42,6 @@ def test_mfma_probe_validation():
     assert L.oases_mfma_probe(1, 1, None, None) == shard.E_ARG
 
 
-def test_feed_probe_validation():
-    L = shard.lib()
-    buf = ctypes.create_string_buffer(16)
-    assert L.oases_feed_probe(3, 1, 1, buf, 65536, buf, None) == shard.E_ARG       # mode
-    assert L.oases_feed_probe(0, 1, 1, buf, 65536 + 16, buf, None) == shard.E_ARG  # size
-    assert L.oases_feed_probe(0, 0, 1, buf, 65536, buf, None) == shard.E_ARG       # grid
-    assert L.oases_feed_probe(0, 1, 1, None, 65536, buf, None) == shard.E_ARG      # source
-
-
 def test_profile_timeline_validation():
     L = shard.lib()
     n = ctypes.c_int32(0)

@@ -8,7 +8,7 @@ import pytest
 
 import gen
 from oracle import blocks, sums
-from helpers import assert_close, gpu_available
+from helpers import assert_close, assert_close_local, gpu_available
 
 pytestmark = pytest.mark.gpu
 
@@ -104,7 +104,8 @@ def test_attention_fwd(variant, d, nb, s, nh, causal):
     f = gen.bf16_bits_to_f64(qkv)
     q, k, v = (blocks.split_heads(f[:, i * a:(i + 1) * a], nb, s, nh, d) for i in range(3))
     o_ref, _ = blocks.attention_fwd(q, k, v, causal)
-    assert_close(gen.bf16_bits_to_f64(to_storage(o)), blocks.merge_heads(o_ref), 2e-2, "O")
+    assert_close_local(gen.bf16_bits_to_f64(to_storage(o)), blocks.merge_heads(o_ref), 2e-2, "O",
+                       block_cols=d)
     sc = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(d)
     if causal:
         sc = np.where(np.triu(np.ones((s, s), bool), 1), -np.inf, sc)
@@ -181,33 +182,52 @@ def test_mfma_probe_runs():
     assert np.isfinite(v).all() and (v != 0).any()
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
-def test_feed_probe_runs(mode):
-    """The operand feed probe moves the bytes it claims through each path:
-    its per-lane checksums equal the XOR of the source words it read (mode 1)
-    or of the LDS vector it left behind (modes 0 and 2), computed on the host."""
-    iters = 3
-    host = (np.arange(1 << 16) % 251).astype(np.uint8)
-    src = torch.from_numpy(host).to("cuda")
-    out = torch.zeros(2 * 256, dtype=torch.int32, device="cuda")
-    nbytes = shard.feed_probe(mode, 2, iters, src, out)
-    torch.cuda.synchronize()
-    assert nbytes == 2 * 4 * 8 * iters * 1024
-    words = host.view(np.uint32)           # 4-byte words of the 64 KB slice (both workgroups read it)
-    want = np.zeros(256, np.uint32)
-    for t in range(256):
-        lane, wave = t % 64, t // 64
-        if mode == 1:
-            acc = np.zeros(4, np.uint32)
-            for i in range(iters):
-                for u in range(8):
-                    unit = ((i * 8 + u) * 4 + wave) % 64
-                    o = (unit * 1024 + lane * 16) // 4
-                    acc ^= words[o:o + 4]
-        else:                               # the LDS holds the slice itself after the walk
-            o = t * 16 // 4
-            acc = words[o:o + 4]
-        want[t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3]
-    got = out.cpu().numpy().view(np.uint32)
-    np.testing.assert_array_equal(got[:256], want)
-    np.testing.assert_array_equal(got[256:], want)
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nb,s,nh,causal", [(1, 1, 1, True), (2, 100, 3, True), (1, 300, 2, False),
+                                            (2, 512, 2, True), (1, 1030, 1, True), (1, 130, 2, False)])
+def test_attention_bwd(variant, d, nb, s, nh, causal):
+    """dQ, dK and dV of the attention backward (delta, dK/dV with dS, dQ from
+    dS) against the float64 definitions, per head and per 64-row block, with
+    O and lse from the GPU forward (both sides see the same bf16 O)."""
+    rng = np.random.default_rng(3 * d + s + 7 * nh + variant)
+    a = nh * d
+    qkv = _bf16_bits(rng, (nb * s, 3 * a))
+    dout = _bf16_bits(rng, (nb * s, a))
+    t = to_device(qkv, gen.BF16, "cuda")
+    do_t = to_device(dout, gen.BF16, "cuda")
+    o = torch.empty(nb * s, a, dtype=torch.bfloat16, device="cuda")
+    s_pad = (s + 63) // 64 * 64
+    lse = torch.empty(nb, nh, s_pad, dtype=torch.float32, device="cuda")
+    dqkv = torch.full((nb * s, 3 * a), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.full((shard.attention_bwd_workspace_bytes(nb, s, nh),), 255, dtype=torch.uint8, device="cuda")
+    shard.set_attention_variant(variant)
+    try:
+        shard.attention_fwd(nb, s, nh, d, causal, t, o, lse)
+        shard.attention_bwd(nb, s, nh, d, causal, t, o, do_t, lse, dqkv, ws)
+        torch.cuda.synchronize()
+    finally:
+        shard.set_attention_variant(0)
+    f = gen.bf16_bits_to_f64(qkv)
+    q, k, v = (blocks.split_heads(f[:, i * a:(i + 1) * a], nb, s, nh, d) for i in range(3))
+    _, p = blocks.attention_fwd(q, k, v, causal)
+    dof = blocks.split_heads(gen.bf16_bits_to_f64(dout), nb, s, nh, d)
+    dq, dk, dv = blocks.attention_bwd(q, k, v, p, dof)
+    got = gen.bf16_bits_to_f64(to_storage(dqkv))
+    for i, (name, ref) in enumerate((("dQ", dq), ("dK", dk), ("dV", dv))):
+        assert_close_local(got[:, i * a:(i + 1) * a], blocks.merge_heads(ref), 2e-2, name, block_cols=d)
+
+
+def test_attention_bwd_rejects_bad_arguments():
+    dev = "cuda"
+    x = torch.zeros(64, dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros(64, dtype=torch.float32, device=dev)
+    need = shard.attention_bwd_workspace_bytes(1, 8, 1)
+    small = torch.zeros(need - 16, dtype=torch.uint8, device=dev)
+    L = shard.lib()
+    ptr = shard._ptr
+    assert L.oases_attention_bwd(1, 8, 1, 96, 1, ptr(x), ptr(x), ptr(x), ptr(lse), ptr(x), ptr(small), need, None) \
+        == shard.E_ARG
+    assert L.oases_attention_bwd(1, 8, 1, 64, 1, ptr(x), ptr(x), ptr(x), ptr(lse), ptr(x), ptr(small),
+                                 need - 16, None) == shard.E_ARG
+    assert "need" in L.oases_last_call_error().decode()

@@ -403,6 +403,32 @@ def test_dropout_mask_rate_and_layout():
     assert (keep != blocks.dropout_keep(T, h, 2, 0, 5, 16384)).any()
 
 
+def test_dropout_scale_is_inverted_dropout():
+    """dropout_residual keeps an element as s / (1 - p) and drops it to 0,
+    checked against scales written out by hand for p = 1/2, 1/4 and 1/8
+    (2, 4/3, 8/7), and against the defining property of inverted dropout:
+    averaged over many independent masks, dropout(s) has mean s."""
+    T, h = 32, 64
+    s = RNG.standard_normal((T, h))
+    x = RNG.standard_normal((T, h))
+    for drop_q, scale in ((32768, 2.0), (16384, 4.0 / 3.0), (8192, 8.0 / 7.0)):
+        keep = blocks.dropout_keep(T, h, 3, 1, 77, drop_q)
+        out = blocks.dropout_residual(x, s, keep, drop_q)
+        assert keep.any() and (~keep).any()
+        np.testing.assert_allclose(out[keep], x[keep] + s[keep] * scale, rtol=1e-15, atol=0)
+        np.testing.assert_array_equal(out[~keep], x[~keep])
+    # expectation over 400 masks (different layers): mean within 5 standard errors of s
+    drop_q, p = 16384, 0.25
+    ones = np.ones((8, 16))
+    acc = np.zeros_like(ones)
+    for layer in range(400):
+        keep = blocks.dropout_keep(8, 16, layer, 0, 99, drop_q)
+        acc += blocks.dropout_residual(np.zeros_like(ones), ones, keep, drop_q)
+    mean = acc / 400
+    se = math.sqrt(p / (1 - p) / 400)  # std of one draw of dropout(1) is sqrt(p / (1 - p))
+    assert np.abs(mean - 1.0).max() < 5 * se
+
+
 def test_layer_norm_matches_torch():
     import torch
     x, w, b = RNG.standard_normal((7, 24)) * 3 + 1, RNG.standard_normal(24), RNG.standard_normal(24)
