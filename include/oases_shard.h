@@ -345,6 +345,22 @@ int oases_attention_bwd(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t c
                         const void *o, const void *dout, const float *lse, void *dqkv, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * oases_attention_bwd with its scratch in a static device array of 48 MiB
+ * instead of a workspace argument.  Each GPU the library runs on holds its
+ * own copy of the array until the process ends; the call allocates nothing.
+ * Arguments, layouts and outputs as oases_attention_bwd.  A problem whose
+ * scratch (oases_attention_bwd_workspace_bytes) exceeds 48 MiB is rejected
+ * with OASES_E_ARG before any launch (message in oases_last_call_error).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams or threads) race and give wrong results; calls ordered
+ * on one stream are safe.  Nothing in the array needs to start at zero: each
+ * call writes every entry it reads. */
+int oases_attention_bwd_noalloc(int32_t nb, int32_t s, int32_t n_h, int32_t d, int32_t causal,
+                                const void *qkv, const void *o, const void *dout, const float *lse,
+                                void *dqkv, void *stream);
+
 /* Message of the last failing call on this thread that takes no context
  * (oases_create and the single-kernel entry points); "" if none. */
 const char *oases_last_call_error(void);

@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "liboases_shard.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["executor.cpp", "gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "attention.hip", "probe.hip"]
+SOURCES = ["executor.cpp", "gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "attention.hip", "probe.hip",
+           "noalloc.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 vector ops stay off (the compiler must not form them)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

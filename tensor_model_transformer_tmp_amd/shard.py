@@ -30,7 +30,8 @@ EXPORTED = ("oases_create", "oases_workspace_bytes", "oases_bind", "oases_set_st
             "oases_sync", "oases_last_error", "oases_destroy", "oases_profile_begin",
             "oases_profile_end", "oases_profile_timeline", "oases_mfma_probe", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
             "oases_attention_variant", "oases_sum_grid_cap", "oases_attention_fwd",
-            "oases_attention_bwd_workspace_bytes", "oases_attention_bwd", "oases_last_call_error")
+            "oases_attention_bwd_workspace_bytes", "oases_attention_bwd", "oases_attention_bwd_noalloc",
+            "oases_last_call_error")
 
 
 class OasesError(RuntimeError):
@@ -95,6 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "oases_attention_fwd": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P]),
         "oases_attention_bwd_workspace_bytes": (ctypes.c_int, [I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]),
         "oases_attention_bwd": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "oases_attention_bwd_noalloc": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, P]),
         "oases_last_call_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -327,3 +329,11 @@ def attention_bwd(nb, s, nh, d, causal, qkv, o, dout, lse, dqkv, workspace, stre
                                           _ptr(dqkv), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(),
                                           _stream_handle(stream)), "oases_attention_bwd")
+
+
+def attention_bwd_noalloc(nb, s, nh, d, causal, qkv, o, dout, lse, dqkv, stream=None):
+    """dQKV of the attention block with the library's static scratch (no
+    workspace argument; problems up to 48 MiB of scratch)."""
+    _check_free(lib().oases_attention_bwd_noalloc(nb, s, nh, d, int(causal), _ptr(qkv), _ptr(o), _ptr(dout),
+                                                  _ptr(lse), _ptr(dqkv), _stream_handle(stream)),
+                "oases_attention_bwd_noalloc")
