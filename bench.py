@@ -511,7 +511,7 @@ def main():
     use_graph = args.issue == "graph"
     cs = dev.compute
 
-    def steps_with_events(n, graph):
+    def steps_with_events(n, graph, mode=mode):
         """n steps, each bracketed by HIP events on the compute stream (the
         step forks the side stream from it and joins it back), with a
         synchronize on both sides of the whole run: (wall s, [ms per step])."""
@@ -553,7 +553,7 @@ def main():
     # kernels, one stream, nothing running beside a launch), events as above
     n_solo = 5
     dev.ctx.profile_begin("all", cap)
-    steps_with_events(n_solo, False)
+    steps_with_events(n_solo, False, "serial_fine")
     tl_solo = dev.ctx.profile_timeline(cap)
     dev.close()
 
