@@ -308,15 +308,31 @@ int oases_gemm_tile_variant(int32_t variant);
  * captured with.  1..65536, else OASES_E_ARG. */
 int oases_sum_grid_cap(int32_t workgroups);
 
+/* Form of the AllReduce-point sum kernel for this process.  Form A keeps the
+ * loads of several 16-byte vectors per thread in flight (fastest alone);
+ * form B takes one vector per thread with all w inputs in flight, in few
+ * enough registers that its waves fit on a CU beside a GEMM workgroup's, so
+ * a sum issued beside the other sub-batch's compute shares CUs with it
+ * instead of taking them.  0 = automatic (the default: form B for the sums
+ * of the overlapped schedules, form A for sums that run alone and for
+ * oases_allreduce_point), 1 = always form A, 2 = always form B.  Both add in
+ * the same order and give the same bits.  Graphs already captured keep the
+ * form they were captured with.  OASES_E_ARG for other values. */
+int oases_sum_variant(int32_t variant);
+
 /* Attention work split for this process.  A workgroup has 4 waves of 32
  * rows each; OWN of them own distinct row tiles (sharing each staged block)
  * and 4/OWN split the walk over the other operand.  With tile pairs a
  * workgroup takes two row tiles, one with a long and one with a short causal
- * walk.  0 = automatic (the default: the largest OWN that gives 256
- * workgroups; for the backward, OWN 1 with pairs when pairs alone give 256
- * workgroups of a causal attention), 1 = OWN 1,
- * 2 = OWN 4, 3 = OWN 2, 4 = OWN 1 with pairs, 5 = OWN 2 with pairs.  For
- * tests and tuning; OASES_E_ARG for other values. */
+ * walk.  0 = automatic (the default: for the forward, 8-wave workgroups
+ * with the largest OWN in {4, 2} (or 1 for d = 64) that gives 256
+ * workgroups, else the largest OWN of 4 waves that does; for the backward,
+ * OWN 1 with pairs when pairs alone give 256 workgroups of a causal
+ * attention, else as the 4-wave forward), 1 = OWN 1, 2 = OWN 4, 3 = OWN 2,
+ * 4 = OWN 1 with pairs, 5 = OWN 2 with pairs; 6, 7, 8: the forward with
+ * 8-wave workgroups and OWN 2, 4, 1 (OWN 1 for d = 64 only; d = 128 runs
+ * OWN 2), the backward automatic.  For tests and tuning; OASES_E_ARG for
+ * other values. */
 int oases_attention_variant(int32_t variant);
 
 /* Causal (causal = 1) or full attention forward over QKV [nb*s, 3a]

@@ -199,10 +199,10 @@ __device__ __forceinline__ void stash(float *red, const f32x16 (&acc)[D / 32], i
 // Sum the SPLIT stashed partials of each owned tile in split order and store
 // them as bf16 at row (row0 + own*32 + q), columns [d0, d0+8) of dst (row
 // stride ld), times scale.  red holds [split][own][D][32] floats.
-template <int D, int OWN, int SPLIT>
+template <int D, int OWN, int SPLIT, int W = NW>
 __device__ __forceinline__ void combine_store(const float *red, bf16_t *dst, int ld, int row0, int nrows,
                                               float scale) {
-  for (int c = threadIdx.x; c < OWN * 32 * (D / 8); c += 64 * NW) {
+  for (int c = threadIdx.x; c < OWN * 32 * (D / 8); c += 64 * W) {
     const int q = c % 32, d0 = ((c / 32) % (D / 8)) * 8, own = c / (32 * (D / 8));
     const int row = row0 + own * 32 + q;
     if (row >= nrows) continue;
@@ -222,15 +222,16 @@ __device__ __forceinline__ void combine_store(const float *red, bf16_t *dst, int
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int D, int OWN>
-struct KvCfg {  // staging of K and V blocks (forward and dQ)
-  static constexpr int SPLIT = NW / OWN;
+template <int D, int OWN, int W = NW>
+struct KvCfg {  // staging of K and V blocks (forward); W waves per workgroup
+  static constexpr int SPLIT = W / OWN;
   static constexpr int UNITS = SPLIT * 2 * Blk<D>::UNITS;  // K and V of SPLIT key blocks per step
-  static_assert(UNITS % NW == 0, "units per wave");
-  static constexpr int DL = UNITS / NW;
+  static_assert(UNITS % W == 0, "units per wave");
+  static constexpr int DL = UNITS / W;
   static constexpr int STAGE_BYTES = SPLIT * 2 * Blk<D>::BYTES;
   static constexpr int STAGES = 3 * STAGE_BYTES <= LDS_BUDGET ? 3 : 2;
-  static constexpr int RED_BYTES = NW * D * 32 * 4 + NW * 2 * 32 * 4;
+  static_assert(2 * STAGE_BYTES <= LDS_BUDGET, "two stages of K and V");
+  static constexpr int RED_BYTES = W * D * 32 * 4 + W * 2 * 32 * 4;
   static constexpr int LDS = STAGES * STAGE_BYTES > RED_BYTES ? STAGES * STAGE_BYTES : RED_BYTES;
 };
 
@@ -248,16 +249,16 @@ __device__ __forceinline__ void dma_clamped(const bf16_t *p, int ld, int row0, i
 // a step is block g = uu / (2 UNITS), K or V, unit uu % UNITS of that block.
 // Lane offsets are relative to the step's first key row, so all units of a
 // step share one scalar base and a unit costs a DMA and an M0 write.
-template <int D, int OWN>
+template <int D, int OWN, int W = NW>
 struct KvStager {
   using B = Blk<D>;
-  using C = KvCfg<D, OWN>;
+  using C = KvCfg<D, OWN, W>;
   uint32_t voff[C::DL];
   int lds[C::DL];  // byte offset of the unit in a stage (uniform)
   __device__ __forceinline__ void init(int wave, int lane, int ld, int a) {
 #pragma unroll
     for (int j = 0; j < C::DL; ++j) {
-      const int uu = j * NW + wave, g = uu / (2 * B::UNITS), which = (uu / B::UNITS) & 1, u = uu % B::UNITS;
+      const int uu = j * W + wave, g = uu / (2 * B::UNITS), which = (uu / B::UNITS) & 1, u = uu % B::UNITS;
       int r, cb;
       B::unit_src(u, lane, r, cb);
       voff[j] = (uint32_t)(((g * RB + r) * ld + which * a) * 2 + cb);
@@ -278,12 +279,12 @@ struct KvStager {
   }
 };
 
-template <int D, int OWN>
-__global__ void __launch_bounds__(64 * NW)
+template <int D, int OWN, int W>
+__global__ void __launch_bounds__(64 * W)
     attn_fwd_kernel(const bf16_t *__restrict__ qkv, bf16_t *__restrict__ out, float *__restrict__ lse,
                     int s, int s_pad, int nh, int causal, float scale_log2, float scale, int pair) {
   using B = Blk<D>;
-  using C = KvCfg<D, OWN>;
+  using C = KvCfg<D, OWN, W>;
   constexpr int SPLIT = C::SPLIT, DL = C::DL;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -295,7 +296,7 @@ __global__ void __launch_bounds__(64 * NW)
   const bf16_t *Qp = qkv + (int64_t)b * s * ld + h * D;
   const bf16_t *Kp = Qp + a;
 
-  KvStager<D, OWN> stg;
+  KvStager<D, OWN, W> stg;
   stg.init(wave, lane, ld, a);
 
   // tiles of this workgroup, heaviest causal walk first: tile ntile-1-x, and
@@ -381,14 +382,14 @@ __global__ void __launch_bounds__(64 * NW)
   //   O = sum_w 2^(m_w - m) O_w / sum_w 2^(m_w - m) l_w   (m in scaled units)
   lds_barrier();
   float *red = reinterpret_cast<float *>(smem);  // [split][own][D][32]
-  float *ml = red + NW * D * 32;                  // [split][own][2][32]
+  float *ml = red + W * D * 32;                   // [split][own][2][32]
   stash<D>(red + (sp * OWN + own) * D * 32, oacc, l32, hl);
   if (hl == 0) {
     ml[((sp * OWN + own) * 2 + 0) * 32 + l32] = m_run;
     ml[((sp * OWN + own) * 2 + 1) * 32 + l32] = l_run;
   }
   lds_barrier();
-  for (int c = threadIdx.x; c < OWN * 32 * (D / 8); c += 64 * NW) {
+  for (int c = threadIdx.x; c < OWN * 32 * (D / 8); c += 64 * W) {
     const int q = c % 32, d0 = ((c / 32) % (D / 8)) * 8, ow = c / (32 * (D / 8));
     const int qq = q0 + ow * 32 + q;
     if (qq >= s) continue;
@@ -784,11 +785,13 @@ __global__ void __launch_bounds__(64 * NW)
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-int g_attn_variant = 0;  // 0 automatic; 1, 2, 3: OWN = 1, 4, 2; 4, 5: OWN = 1, 2 with tile pairs
+int g_attn_variant = 0;  // 0 automatic; 1, 2, 3: OWN = 1, 4, 2; 4, 5: OWN = 1, 2 with tile pairs;
+                         // 6, 7, 8: forward with 8 waves, OWN = 2, 4, 1
 
 struct AttnPlan {
   int own;
-  int pair;  // 1: a workgroup takes two tiles, one of the longest and one of the shortest causal walks
+  int pair;   // 1: a workgroup takes two tiles, one of the longest and one of the shortest causal walks
+  int waves;  // waves per workgroup (the forward also runs 8)
 };
 
 // OWN (waves of a workgroup that own distinct 32-row tiles): the largest
@@ -799,19 +802,29 @@ struct AttnPlan {
 // longest walk twice the average).  The forward keeps shared staging (OWN 2)
 // instead: measured on MI355X, pairs help the backward by up to a fifth at
 // s = 2048 and slow the forward.
-AttnPlan pick_plan(int s, int nbh, int causal, bool bwd) {
+AttnPlan pick_plan(int s, int nbh, int causal, bool bwd, int d = 128) {
   switch (g_attn_variant) {
-    case 1: return {1, 0};
-    case 2: return {4, 0};
-    case 3: return {2, 0};
-    case 4: return {1, 1};
-    case 5: return {2, 1};
+    case 1: return {1, 0, NW};
+    case 2: return {4, 0, NW};
+    case 3: return {2, 0, NW};
+    case 4: return {1, 1, NW};
+    case 5: return {2, 1, NW};
+    case 6: if (!bwd) return {2, 0, 8}; break;
+    case 7: if (!bwd) return {4, 0, 8}; break;
+    case 8: if (!bwd) return {d == 64 ? 1 : 2, 0, 8}; break;  // 8 waves of one tile: d = 64 only (LDS)
     default: break;
   }
-  if (bwd && causal && (int64_t)((s + 31) / 32 / 2) * nbh >= 256) return {1, 1};
+  if (bwd && causal && (int64_t)((s + 31) / 32 / 2) * nbh >= 256) return {1, 1, NW};
+  if (!bwd) {
+    // forward: 8-wave workgroups (two waves per SIMD; the walk split four
+    // or eight ways) when they alone give 256 workgroups
+    for (int own : {4, 2})
+      if ((int64_t)((s + 32 * own - 1) / (32 * own)) * nbh >= 256) return {own, 0, 8};
+    if (d == 64 && (int64_t)((s + 31) / 32) * nbh >= 256) return {1, 0, 8};
+  }
   for (int own : {4, 2})
-    if ((int64_t)((s + 32 * own - 1) / (32 * own)) * nbh >= 256) return {own, 0};
-  return {1, 0};
+    if ((int64_t)((s + 32 * own - 1) / (32 * own)) * nbh >= 256) return {own, 0, NW};
+  return {1, 0, NW};
 }
 
 // workgroups along a (sequence, head): one per tile, or one per pair of tiles
@@ -820,12 +833,12 @@ int tile_wgs(int s, int own, int pair) {
   return pair ? (ntile + 1) / 2 : ntile;
 }
 
-template <int D, int OWN>
+template <int D, int OWN, int W = NW>
 hipError_t fwd_launch(int nb, int s, int nh, int causal, int pair, const void *qkv, void *o, float *lse,
                       hipStream_t st) {
   const float scale = 1.f / sqrtf((float)D);
   const dim3 grid(tile_wgs(s, OWN, pair), nb * nh);
-  OASES_LAUNCH((attn_fwd_kernel<D, OWN>), grid, dim3(64 * NW), st, static_cast<const bf16_t *>(qkv),
+  OASES_LAUNCH((attn_fwd_kernel<D, OWN, W>), grid, dim3(64 * W), st, static_cast<const bf16_t *>(qkv),
                static_cast<bf16_t *>(o), lse, s, attn_lse_stride(s), nh, causal, scale * LOG2E, scale, pair);
   return hipSuccess;
 }
@@ -851,7 +864,16 @@ hipError_t bwd_launch(int nb, int s, int nh, int causal, int pair, const void *q
 
 template <int D>
 hipError_t fwd_d(int nb, int s, int nh, int causal, const void *qkv, void *o, float *lse, hipStream_t st) {
-  const AttnPlan pl = pick_plan(s, nb * nh, causal, false);
+  const AttnPlan pl = pick_plan(s, nb * nh, causal, false, D);
+  if (pl.waves == 8) {
+    switch (pl.own) {
+      case 4: return fwd_launch<D, 4, 8>(nb, s, nh, causal, 0, qkv, o, lse, st);
+      case 2: return fwd_launch<D, 2, 8>(nb, s, nh, causal, 0, qkv, o, lse, st);
+      default:
+        if constexpr (D == 64) return fwd_launch<D, 1, 8>(nb, s, nh, causal, 0, qkv, o, lse, st);
+        return fwd_launch<D, 2, 8>(nb, s, nh, causal, 0, qkv, o, lse, st);
+    }
+  }
   switch (pl.own) {
     case 4: return fwd_launch<D, 4>(nb, s, nh, causal, pl.pair, qkv, o, lse, st);
     case 2: return fwd_launch<D, 2>(nb, s, nh, causal, pl.pair, qkv, o, lse, st);

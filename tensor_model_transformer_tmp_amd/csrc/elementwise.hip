@@ -72,6 +72,36 @@ __global__ void __launch_bounds__(SUM_NT)
   }
 }
 
+// Lean form of the same sum: one vector per thread per iteration, its NP + 1
+// loads in flight, so few registers that its waves fit on a CU beside a
+// GEMM workgroup's (the GEMM holds most of the register file but leaves the
+// memory pipeline mostly idle).  Same adds in the same order: bit-identical.
+template <int NP, bool TAIL>
+__global__ void __launch_bounds__(SUM_NT)
+    allreduce_bf16_lean_kernel(const uint4 *__restrict__ own, const bf16_t *__restrict__ peers,
+                               int64_t peer_stride, uint4 *__restrict__ out, int64_t nvec, DropRes t) {
+  for (int64_t v = (int64_t)blockIdx.x * SUM_NT + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * SUM_NT) {
+    uint4 x[NP + 1];
+#pragma unroll
+    for (int k = 0; k <= NP; ++k) {
+      const uint4 *src = k == 0 ? own : reinterpret_cast<const uint4 *>(peers + (int64_t)(k - 1) * peer_stride);
+      x[k] = stream_load(src + v);
+    }
+    float acc[8] = {lo_f32(x[0].x), hi_f32(x[0].x), lo_f32(x[0].y), hi_f32(x[0].y),
+                    lo_f32(x[0].z), hi_f32(x[0].z), lo_f32(x[0].w), hi_f32(x[0].w)};
+#pragma unroll
+    for (int k = 1; k <= NP; ++k) {
+      const uint4 b = x[k];
+      acc[0] += lo_f32(b.x); acc[1] += hi_f32(b.x); acc[2] += lo_f32(b.y); acc[3] += hi_f32(b.y);
+      acc[4] += lo_f32(b.z); acc[5] += hi_f32(b.z); acc[6] += lo_f32(b.w); acc[7] += hi_f32(b.w);
+    }
+    if constexpr (TAIL)
+      drop_res8(acc, reinterpret_cast<const uint4 *>(t.res)[v], v, t.seed, t.layer, t.sb, t.thr, t.scale, t.drop);
+    out[v] = make_uint4(cvt_pk(acc[0], acc[1]), cvt_pk(acc[2], acc[3]), cvt_pk(acc[4], acc[5]),
+                        cvt_pk(acc[6], acc[7]));
+  }
+}
+
 // more peers than the unrolled kernels cover: a runtime loop over the peers
 __global__ void __launch_bounds__(SUM_NT)
     allreduce_bf16_many_kernel(const uint4 *__restrict__ own, const bf16_t *__restrict__ peers,
@@ -479,9 +509,16 @@ __global__ void __launch_bounds__(SUM_NT)
 }  // namespace
 
 int g_sum_grid_cap = 512;  // workgroups of the AllReduce-point sum (tunable)
+int g_sum_variant = 0;     // 0 automatic (per call site), 1 several vectors per thread, 2 lean
+
+int allreduce_form(bool beside_compute) {
+  if (g_sum_variant == 1) return 0;
+  if (g_sum_variant == 2) return 1;
+  return beside_compute ? 1 : 0;
+}
 
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
-                           int n_peers, void *out, int64_t n, hipStream_t s, const DropRes *tail) {
+                           int n_peers, void *out, int64_t n, hipStream_t s, const DropRes *tail, int form) {
   if (n <= 0) return hipSuccess;
   if (tail && tail->res && !bf16) return hipErrorInvalidValue;
   const DropRes t = tail ? *tail : DropRes{};
@@ -498,6 +535,23 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
                  static_cast<const float *>(peers), peer_stride, n_peers, static_cast<float4 *>(out), nvec);
     return hipSuccess;
   }
+  if (form == 1 && n_peers <= 7) {
+    // beside compute kernels: half the grid cap (measured at the 8192-hidden
+    // pair: 256 workgroups leave the sums 96% hidden, 512-2048 about 90%)
+    const int64_t want1 = (nvec + SUM_NT - 1) / SUM_NT, cap1 = g_sum_grid_cap < 2 ? 1 : g_sum_grid_cap / 2;
+    const dim3 grid1((unsigned)(want1 < cap1 ? want1 : cap1));
+    switch (n_peers) {
+#define OASES_SUM_CASE(NP)                                                                                  \
+  case NP:                                                                                                  \
+    if (t.res) OASES_LAUNCH((allreduce_bf16_lean_kernel<NP, true>), grid1, dim3(SUM_NT), s, o, p, peer_stride, y, nvec, t); \
+    else OASES_LAUNCH((allreduce_bf16_lean_kernel<NP, false>), grid1, dim3(SUM_NT), s, o, p, peer_stride, y, nvec, t); \
+    break;
+      OASES_SUM_CASE(0) OASES_SUM_CASE(1) OASES_SUM_CASE(2) OASES_SUM_CASE(3)
+      OASES_SUM_CASE(4) OASES_SUM_CASE(5) OASES_SUM_CASE(6) OASES_SUM_CASE(7)
+#undef OASES_SUM_CASE
+    }
+    return hipSuccess;
+  }
   switch (n_peers) {
 #define OASES_SUM_CASE(NP) \
   case NP: OASES_LAUNCH(allreduce_bf16_kernel<NP>, grid, dim3(SUM_NT), s, o, p, peer_stride, y, nvec, t); break;
@@ -511,6 +565,7 @@ hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_
 }
 
 void allreduce_set_grid_cap(int cap) { g_sum_grid_cap = cap; }
+void allreduce_set_variant(int v) { g_sum_variant = v; }
 
 int allreduce_fused_wgs(int64_t nvec) {
   // half the standalone grid cap: beside a GEMM's tiles, a larger sum grid

@@ -393,7 +393,11 @@ struct Exec {
       return OASES_OK;
     }
     if (int r = prof_begin(KC_SUM, s)) return r;
-    HIPX(allreduce_point(bf16(), own, pr, (int64_t)D().T * D().h, D().w - 1, out, (int64_t)D().T * D().h, s, &t));
+    // a sum issued beside the other sub-batch's compute (side stream, or a
+    // stream per sub-batch) takes the low-register form that shares CUs
+    const int form = allreduce_form(overlap || by_sb);
+    HIPX(allreduce_point(bf16(), own, pr, (int64_t)D().T * D().h, D().w - 1, out, (int64_t)D().T * D().h, s, &t,
+                         form));
     return prof_end(KC_SUM, s);
   }
 
@@ -907,7 +911,7 @@ int oases_allreduce_point(int32_t dtype, const void *own, const void *peers, int
   if (!own || !out) return OASES_E_ARG;
   if (!aligned16(own) || !aligned16(out) || (n_peers > 0 && !aligned16(peers))) return OASES_E_ALIGN;
   const hipError_t e = allreduce_point(dtype == OASES_BF16, own, peers, peer_stride, n_peers, out, n,
-                                       static_cast<hipStream_t>(stream));
+                                       static_cast<hipStream_t>(stream), nullptr, allreduce_form(false));
   return e == hipSuccess ? OASES_OK : OASES_E_HIP;
 }
 
@@ -957,8 +961,14 @@ int oases_sum_grid_cap(int32_t workgroups) {
   return OASES_OK;
 }
 
+int oases_sum_variant(int32_t variant) {
+  if (variant < 0 || variant > 2) return call_fail(OASES_E_ARG, "oases_sum_variant: 0, 1 or 2");
+  allreduce_set_variant(variant);
+  return OASES_OK;
+}
+
 int oases_attention_variant(int32_t variant) {
-  if (variant < 0 || variant > 5) return OASES_E_ARG;
+  if (variant < 0 || variant > 8) return OASES_E_ARG;
   attention_set_variant(variant);
   return OASES_OK;
 }

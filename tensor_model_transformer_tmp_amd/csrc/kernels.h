@@ -118,9 +118,16 @@ void gemm_bf16_set_variant(int v);
 // dense bf16 MFMA throughput probe: `workgroups` x 4 waves, each issuing
 // 4 * iters v_mfma_f32_32x32x16_bf16; out holds workgroups * 256 floats
 hipError_t mfma_probe(int workgroups, int iters, float *out, hipStream_t s);
+// form 0: several 16-byte vectors per thread in flight (fastest alone); 1:
+// one vector per thread with all inputs in flight and few registers, so the
+// sum's waves fit on CUs beside a GEMM workgroup's (bf16, up to 7 peers).
+// Both give the same bits.
 hipError_t allreduce_point(bool bf16, const void *own, const void *peers, int64_t peer_stride,
                            int n_peers, void *out, int64_t n, hipStream_t s,
-                           const DropRes *tail = nullptr);
+                           const DropRes *tail = nullptr, int form = 0);
+// the form to use for a sum that runs beside compute kernels or alone (the
+// process setting of oases_sum_variant, else that choice)
+int allreduce_form(bool beside_compute);
 
 // ---- full transformer block (bf16) ----
 // z = LayerNorm(x) * w + b per row of x [rows, h] (biased variance, eps)
@@ -140,6 +147,9 @@ int64_t layer_norm_partial_floats(int rows, int h);
 hipError_t dropout_bwd(const void *g, void *out, int64_t n, const DropRes &t, hipStream_t s);
 // largest grid (workgroups) of the AllReduce-point kernel
 void allreduce_set_grid_cap(int cap);
+// form of the AllReduce-point kernel for this process: 0 automatic, 1 always
+// several vectors per thread, 2 always one vector per thread
+void allreduce_set_variant(int v);
 // workgroups that run an AllReduce point of nvec 8-element vectors fused into
 // a GEMM launch (a multiple of 8, at most half the grid cap)
 int allreduce_fused_wgs(int64_t nvec);

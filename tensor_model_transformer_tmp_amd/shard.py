@@ -29,7 +29,7 @@ EXPORTED = ("oases_create", "oases_workspace_bytes", "oases_bind", "oases_set_st
             "layer_fwd", "layer_bwd_recompute", "schedule_step", "oases_schedule_ops",
             "oases_sync", "oases_last_error", "oases_destroy", "oases_profile_begin",
             "oases_profile_end", "oases_profile_timeline", "oases_mfma_probe", "oases_allreduce_point", "oases_gemm", "oases_gemm_tile_variant",
-            "oases_attention_variant", "oases_sum_grid_cap", "oases_attention_fwd",
+            "oases_attention_variant", "oases_sum_grid_cap", "oases_sum_variant", "oases_attention_fwd",
             "oases_attention_bwd_workspace_bytes", "oases_attention_bwd", "oases_attention_bwd_noalloc",
             "oases_last_call_error")
 
@@ -93,6 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "oases_gemm_tile_variant": (ctypes.c_int, [I32]),
         "oases_attention_variant": (ctypes.c_int, [I32]),
         "oases_sum_grid_cap": (ctypes.c_int, [I32]),
+        "oases_sum_variant": (ctypes.c_int, [I32]),
         "oases_attention_fwd": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P]),
         "oases_attention_bwd_workspace_bytes": (ctypes.c_int, [I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]),
         "oases_attention_bwd": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -304,6 +305,10 @@ def set_gemm_tile_variant(v: int):
 
 def set_sum_grid_cap(workgroups: int):
     _check_free(lib().oases_sum_grid_cap(workgroups), "oases_sum_grid_cap")
+
+
+def set_sum_variant(v: int):
+    _check_free(lib().oases_sum_variant(v), "oases_sum_variant")
 
 
 def set_attention_variant(v: int):

@@ -23,10 +23,13 @@ def _bf16_bits(rng, shape, std=1.0):
     return gen._f32_to_bf16_bits(v).reshape(shape)
 
 
+@pytest.mark.parametrize("form", [1, 2])
 @pytest.mark.parametrize("dtype", [gen.BF16, gen.F32])
-@pytest.mark.parametrize("n,n_peers", [(8, 1), (4096 * 8 + 24, 0), (4096 * 8 + 24, 3),
+@pytest.mark.parametrize("n,n_peers", [(8, 1), (4096 * 8 + 24, 0), (4096 * 8 + 24, 3), (4096 * 8 + 24, 5),
                                         (1 << 20, 7), (3 * 2048 * 1024, 3)])
-def test_allreduce_point_bit_exact(dtype, n, n_peers):
+def test_allreduce_point_bit_exact(dtype, n, n_peers, form):
+    """Both forms of the sum kernel (several vectors per thread in flight, or
+    one) against the float32 sequential sum, bit for bit."""
     rng = np.random.default_rng(n + n_peers)
     mk = (lambda s: _bf16_bits(rng, s)) if dtype == gen.BF16 else \
         (lambda s: rng.standard_normal(s).astype(np.float32))
@@ -35,8 +38,12 @@ def test_allreduce_point_bit_exact(dtype, n, n_peers):
     dev = "cuda"
     t_own, t_peers = to_device(own, dtype, dev), to_device(peers, dtype, dev)
     out = torch.empty_like(t_own)
-    shard.allreduce_point(dtype, t_own, t_peers, n_peers, out)
-    torch.cuda.synchronize()
+    shard.set_sum_variant(form)
+    try:
+        shard.allreduce_point(dtype, t_own, t_peers, n_peers, out)
+        torch.cuda.synchronize()
+    finally:
+        shard.set_sum_variant(0)
     want = sums.allreduce_point_storage(own, [peers[k] for k in range(n_peers)], dtype == gen.BF16)
     np.testing.assert_array_equal(to_storage(out), want)
 
@@ -83,7 +90,7 @@ def test_gemm_fwd_f32():
     assert_close(c.cpu().numpy(), blocks.gelu(ref), 1e-6, "gelu")
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("nb,s,nh,causal", [(1, 1, 1, True), (2, 100, 3, True), (1, 300, 2, False),
                                             (2, 512, 2, True), (1, 1030, 1, True)])
