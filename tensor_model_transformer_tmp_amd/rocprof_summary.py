@@ -199,13 +199,15 @@ _LETTER = {"gemm_fwd": "F", "gemm_dx": "X", "gemm_dw": "W", "attn_fwd": "a", "at
            "sum": "S", "colsum": "c", "ln_fwd": "n", "ln_bwd": "m", "dropout_bwd": "d"}
 
 
-def timed_trace_rows(path: str, steps: int, warmup: int):
-    """The classified dispatches of the plain timed steps of a kernel trace of
-    ``bench.py --study trace``, which runs ``warmup`` steps, ``steps`` plain
-    steps and ``steps`` steps with events on every launch, and nothing else
-    of the library: its classified dispatches are warmup + 2 steps equal steps."""
+def timed_trace_rows(path: str, steps: int, warmup: int, total=None):
+    """The classified dispatches of ``steps`` steps after the first ``warmup``
+    of a kernel trace whose classified dispatches are ``total`` equal steps
+    (every step of one workload issues the same kernels).  ``total`` defaults
+    to warmup + 2 steps: ``bench.py --study trace`` runs ``warmup`` steps,
+    ``steps`` plain steps and ``steps`` steps with events on every launch, and
+    nothing else of the library."""
     rows = [r for r in _trace_rows(path) if r[3] is not None]
-    per_step = len(rows) // (warmup + 2 * steps)
+    per_step = len(rows) // (total if total else warmup + 2 * steps)
     return rows[warmup * per_step:(warmup + steps) * per_step]
 
 
@@ -263,10 +265,10 @@ def overlap_report(rows, steps: int, width: int = 120, unit: float = 1e3) -> tup
     return fig, "\n".join(out)
 
 
-def timeline(path: str, steps: int, warmup: int, width: int = 120) -> str:
+def timeline(path: str, steps: int, warmup: int, width: int = 120, total=None) -> str:
     """Hidden-sum figures over the timed steps of a kernel trace and a text
     chart of one step."""
-    rows = timed_trace_rows(path, steps, warmup)
+    rows = timed_trace_rows(path, steps, warmup, total)
     if not rows:
         return "no classified kernels in the trace"
     return overlap_report(rows, steps, width)[1]
@@ -338,6 +340,8 @@ def main(argv=None):
     t.add_argument("--steps", type=int, required=True)
     t.add_argument("--warmup", type=int, required=True)
     t.add_argument("--width", type=int, default=120)
+    t.add_argument("--total-steps", type=int, default=None,
+                   help="steps in the whole trace (default: warmup + 2 steps, the --study trace layout)")
     m = sub.add_parser("mfma")
     m.add_argument("csv")
     m.add_argument("--workload", default=None)
@@ -359,7 +363,7 @@ def main(argv=None):
         print(stats_table(a.csv))
         return 0
     if a.cmd == "timeline":
-        print(timeline(a.csv, a.steps, a.warmup, a.width))
+        print(timeline(a.csv, a.steps, a.warmup, a.width, a.total_steps))
         return 0
     if a.cmd == "mfma":
         print(mfma_table(a.csv, _class_work_per_launch(a.workload) if a.workload else None))
