@@ -322,12 +322,18 @@ def study_peaks(reps=10):
     del a, b
     # 128 MiB per buffer; then one sub-batch's point of the 8192-hidden pair
     # (2048 x 8192 bf16 = 32 MiB per buffer, 7 peers)
+    # both forms of the sum kernel: A (several vectors per thread in flight,
+    # the form for sums that run alone) and B (one vector per thread, few
+    # registers: the form for sums beside compute)
     for peers, m, name in ((3, 64 << 20, "sum_3_peers_128MiB_each"), (7, 64 << 20, "sum_7_peers_128MiB_each"),
                            (7, 2048 * 8192, "sum_7_peers_2048x8192")):
         own = torch.ones(m, dtype=torch.bfloat16, device=dev)
         pr = torch.ones(peers, m, dtype=torch.bfloat16, device=dev)
         y = torch.empty_like(own)
-        out[name] = timed(lambda: shard.allreduce_point(shard.BF16, own, pr, peers, y), (peers + 2) * 2 * m)
+        for form, tag in ((1, ""), (2, "_form_b")):
+            shard.set_sum_variant(form)
+            out[name + tag] = timed(lambda: shard.allreduce_point(shard.BF16, own, pr, peers, y), (peers + 2) * 2 * m)
+        shard.set_sum_variant(0)
         del own, pr, y
     torch.cuda.empty_cache()
     return {"study": "peaks", "reps": reps, "mfma_bf16_peak_TFLOP/s": MFMA_BF16_PEAK_TFLOPS, "mfma_probe": mfma,
