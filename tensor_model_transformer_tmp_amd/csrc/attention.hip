@@ -6,10 +6,11 @@
 // lse and delta are stored per (sequence, head) with a row stride of
 // s_pad = s rounded up to 64.
 //
-// Work split.  Every kernel runs 4-wave workgroups.  A wave owns 32 rows
-// (queries for the forward and dQ, keys for dK/dV) and walks 32-row blocks of
-// the other operand, staged in LDS by the gfx950 LDS DMA STAGES-1 steps
-// ahead.  The four waves are OWN x SPLIT: OWN waves own different 32-row
+// Work split.  The backward kernels run 4-wave workgroups, the forward 4 or
+// 8 (two waves per SIMD where 8-wave workgroups alone give 256).  A wave owns
+// 32 rows (queries for the forward and dQ, keys for dK/dV) and walks 32-row
+// blocks of the other operand, staged in LDS by the gfx950 LDS DMA STAGES-1
+// steps ahead.  The waves are OWN x SPLIT: OWN waves own different 32-row
 // tiles and share the staged blocks; SPLIT waves own the same tile and take
 // every SPLIT-th block of the walk, and their partial results are combined
 // through LDS in wave order at the end (a fixed order: results are
@@ -17,7 +18,14 @@
 // workgroups, so short sequences with few heads split the walk instead of
 // leaving CUs idle.  Causal walks grow (forward, dQ) or shrink (dK/dV) with
 // the tile index; when there are enough tiles, a backward workgroup takes
-// two, one from each end, so all workgroups carry the same work.
+// two, one from each end, so all workgroups carry the same work.  Workgroup
+// indices are permuted so that each XCD serves whole heads (wg_coords).
+//
+// The dK/dV kernel keeps its key tile's K and V in LDS (fragment-major, read
+// with immediate offsets) rather than in registers, and addresses the staged
+// Q and dO blocks through one base register each (the swizzle is an XOR):
+// its dK and dV accumulators fill half the register file, and the rest must
+// hold fragments in flight rather than hoisted addresses.
 //
 // Layout of a staged 32 x D block: row-major, 16-byte chunk c of row k at
 // c ^ swz(k).  The swizzle keeps both reads conflict-free on the 64-bank LDS:
@@ -88,6 +96,21 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// Workgroup coordinates of a (tiles x sequence-heads) grid, permuted so that
+// the (sequence, head) index varies fastest over consecutive workgroups.
+// Consecutive workgroups go to the 8 XCDs in turn, so when the number of
+// (sequence, head) pairs is a multiple of 8 each XCD serves whole heads and
+// its L2 holds their operands, instead of every XCD streaming every head.
+__device__ __forceinline__ void wg_coords(int &x, int &bh) {
+  const int lin = (int)(blockIdx.y * gridDim.x + blockIdx.x), nbh = (int)gridDim.y;
+  bh = lin % nbh;
+  x = lin / nbh;
+}
+// 16 bytes of LDS at a 32-bit LDS byte address
+__device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr);
+}
 
 // Make the compiler wait for (and keep) values loaded from global memory
 // before the walk starts.  The LDS DMA is invisible to the compiler's wait
@@ -155,6 +178,37 @@ struct Blk {
       const int k = k_lo + hl * 8 + r * 4 + (i >> 2);
       const bf16_t *p = blk + k * D + (((n >> 3) ^ swz(k)) << 3) + (n & 7);
       v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(lds_void_t *)p);
+    }
+    const uint2 lo = __builtin_bit_cast(uint2, v[0]), hi = __builtin_bit_cast(uint2, v[1]);
+    return as_frag(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+
+  // The same reads from 32-bit LDS byte addresses.  The chunk swizzle is an
+  // XOR, so the address of a lane's row fragment kk is its kk = 0 address
+  // XOR (kk << 5), and that of a transposed fragment (column tile t, rows
+  // 16 hh .. 16 hh + 15, half r of the read) is its (0, 0, 0) address XOR a
+  // lane-independent mask, plus hh and r row offsets that become immediate
+  // offsets of the read.  One base register per staged block serves every
+  // fragment of it (a brute-force check over all lanes of these identities
+  // is in the tests).
+  __device__ __forceinline__ static uint32_t frag_base(uint32_t blk, int row, int hl) {
+    return blk + row * D * 2 + ((hl ^ swz(row)) << 4);
+  }
+  __device__ __forceinline__ static bf16x8 frag_at(uint32_t base, int kk) {
+    return lds_frag(base ^ (uint32_t)(kk << 5));
+  }
+  __device__ __forceinline__ static uint32_t frag_t_base(uint32_t blk, int hl) {
+    const int lane = threadIdx.x & 63, i = lane & 15;
+    const int n = (lane & 31) - i + 4 * (i & 3), k = hl * 4 + (i >> 2);
+    return blk + k * D * 2 + ((((n >> 3) ^ swz(k)) << 3) + (n & 7)) * 2;
+  }
+  static constexpr uint32_t tmask(int t, int r) { return D == 128 ? ((t << 6) ^ (r << 5)) : (((t ^ r) & 1) << 6); }
+  __device__ __forceinline__ static bf16x8 frag_t_at(uint32_t base, int t, int hh) {
+    v4i16 v[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t a = (base ^ tmask(t, r)) + (uint32_t)((hh * 16 + r * 8) * D * 2);
+      v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(uintptr_t)a);
     }
     const uint2 lo = __builtin_bit_cast(uint2, v[0]), hi = __builtin_bit_cast(uint2, v[1]);
     return as_frag(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -291,7 +345,9 @@ __global__ void __launch_bounds__(64 * W)
   const int l32 = lane & 31, hl = lane >> 5;
   const int own = wave % OWN, sp = wave / OWN;
   const int ntile = (s + 32 * OWN - 1) / (32 * OWN);
-  const int bh = blockIdx.y, b = bh / nh, h = bh % nh;
+  int wx, bh;
+  wg_coords(wx, bh);
+  const int b = bh / nh, h = bh % nh;
   const int a = nh * D, ld = 3 * a;
   const bf16_t *Qp = qkv + (int64_t)b * s * ld + h * D;
   const bf16_t *Kp = Qp + a;
@@ -302,8 +358,8 @@ __global__ void __launch_bounds__(64 * W)
   // tiles of this workgroup, heaviest causal walk first: tile ntile-1-x, and
   // with pairing also tile x (equal work per workgroup)
   for (int rep = 0; rep < 1 + pair; ++rep) {
-  const int tile = rep == 0 ? ntile - 1 - (int)blockIdx.x : (int)blockIdx.x;
-  if (rep == 1 && tile >= ntile - 1 - (int)blockIdx.x) break;  // odd count: the middle tile is alone
+  const int tile = rep == 0 ? ntile - 1 - wx : wx;
+  if (rep == 1 && tile >= ntile - 1 - wx) break;  // odd count: the middle tile is alone
   if (rep == 1) lds_barrier();  // the previous tile's combine has read the LDS
   const int q0 = tile * 32 * OWN;
   const int qw0 = q0 + own * 32, qi = qw0 + l32;
@@ -431,31 +487,43 @@ struct DkdvCfg {
   static constexpr int DL = 2 * QU + 1;                   // + one lse/delta (or padding) unit
   static constexpr int BLOCK_BYTES = 2 * Blk<D>::BYTES + 1024;
   static constexpr int STAGE_BYTES = SPLIT * BLOCK_BYTES + 1024;  // + a sink for padding units
-  static constexpr int STAGES = 3 * STAGE_BYTES <= LDS_BUDGET ? 3 : 2;
+  // K and V of the workgroup's OWN key tiles, staged once per tile above the ring
+  static constexpr int KV_BYTES = OWN * 2 * Blk<D>::BYTES;
+  static constexpr int KVU = KV_BYTES / 1024 / NW;  // their DMA units per wave
+  static_assert(KV_BYTES % (1024 * NW) == 0, "K/V units per wave");
+  static constexpr int STAGES = 3 * STAGE_BYTES + KV_BYTES <= LDS_BUDGET ? 3 : 2;
+  static_assert(2 * STAGE_BYTES + KV_BYTES <= LDS_BUDGET, "two stages and the key tiles");
+  static constexpr int KV_OFF = STAGES * STAGE_BYTES;
   static constexpr int RED_BYTES = NW * D * 32 * 4;
-  static constexpr int LDS = STAGES * STAGE_BYTES > RED_BYTES ? STAGES * STAGE_BYTES : RED_BYTES;
+  static constexpr int LDS = KV_OFF + KV_BYTES > RED_BYTES ? KV_OFF + KV_BYTES : RED_BYTES;
+  // a wave's consecutive DMA units are JROWS rows apart in the staged rows
+  static constexpr int JROWS = NW * 1024 / (2 * D);
 };
 
 // Q and dO of SPLIT consecutive query blocks per step, and their lse and
 // delta.  Q unit j of a wave is unit qu = j*NW + wave of the step (block
 // qu / UNITS); dO units likewise; wave w < SPLIT also stages the lse (lanes
 // 0-7) and delta (lanes 8-15) of block w, other waves a padding unit, so
-// every wave issues DL units per step.
+// every wave issues DL units per step.  The step's rows are consecutive in
+// memory, so a lane's source row in unit j is j*JROWS plus that of unit 0,
+// at the same swizzled column: one lane offset per tensor, and a scalar
+// base per unit.
 template <int D, int OWN>
 struct DkdvStager {
   using B = Blk<D>;
   using C = DkdvCfg<D, OWN>;
-  uint32_t qoff[C::QU], ooff[C::QU];
-  int qlds[C::QU];  // byte offset of Q unit j in a stage (its dO unit: + B::BYTES)
+  uint32_t qoff, ooff;  // lane byte offset of unit 0 from the step's first row (Q, dO)
+  int qlds[C::QU];      // byte offset of Q unit j in a stage (its dO unit: + B::BYTES)
   __device__ __forceinline__ void init(int wave, int lane, int ld, int a) {
+    const int byte = wave * 1024 + lane * 16;  // unit 0 of this wave lies in block 0
+    const int r = byte / (2 * D), slot = (byte % (2 * D)) >> 4;
+    const int cb = (slot ^ B::swz(r)) << 4;
+    qoff = (uint32_t)(r * ld * 2 + cb);
+    ooff = (uint32_t)(r * a * 2 + cb);
 #pragma unroll
     for (int j = 0; j < C::QU; ++j) {
-      const int qu = j * NW + wave, g = qu / B::UNITS, u = qu % B::UNITS;
-      int r, cb;
-      B::unit_src(u, lane, r, cb);
-      qoff[j] = (uint32_t)((g * RB + r) * ld * 2 + cb);
-      ooff[j] = (uint32_t)((g * RB + r) * a * 2 + cb);
-      qlds[j] = g * C::BLOCK_BYTES + u * 1024;
+      const int qu = j * NW + wave;
+      qlds[j] = (qu / B::UNITS) * C::BLOCK_BYTES + (qu % B::UNITS) * 1024;
     }
   }
   // query rows [row0, row0 + SPLIT*RB); stage: LDS byte address of the stage
@@ -465,14 +533,16 @@ struct DkdvStager {
     if (row0 + C::SPLIT * RB <= s) {
       const bf16_t *bq = Qp + (int64_t)row0 * ld, *bo = dOp + (int64_t)row0 * a;
 #pragma unroll
-      for (int j = 0; j < C::QU; ++j) dma16_s(bq, qoff[j], stage + qlds[j]);
+      for (int j = 0; j < C::QU; ++j) dma16_s(bq + (int64_t)j * C::JROWS * ld, qoff, stage + qlds[j]);
 #pragma unroll
-      for (int j = 0; j < C::QU; ++j) dma16_s(bo, ooff[j], stage + qlds[j] + B::BYTES);
+      for (int j = 0; j < C::QU; ++j) dma16_s(bo + (int64_t)j * C::JROWS * a, ooff, stage + qlds[j] + B::BYTES);
     } else {
 #pragma unroll
-      for (int j = 0; j < C::QU; ++j) dma_clamped(Qp, ld, row0, s, qoff[j], stage + qlds[j]);
+      for (int j = 0; j < C::QU; ++j)
+        dma_clamped(Qp, ld, row0, s, qoff + (uint32_t)(j * C::JROWS * ld * 2), stage + qlds[j]);
 #pragma unroll
-      for (int j = 0; j < C::QU; ++j) dma_clamped(dOp, a, row0, s, ooff[j], stage + qlds[j] + B::BYTES);
+      for (int j = 0; j < C::QU; ++j)
+        dma_clamped(dOp, a, row0, s, ooff + (uint32_t)(j * C::JROWS * a * 2), stage + qlds[j] + B::BYTES);
     }
     if (wave < C::SPLIT) {  // lse and delta rows are padded to s_pad
       const int i = lane & 15, r = min(row0 + wave * RB, s_pad - RB) + 4 * (i & 7);
@@ -499,13 +569,15 @@ __global__ void __launch_bounds__(64 * NW)
   const int ntile = (s + 32 * OWN - 1) / (32 * OWN);
   // tiles of this workgroup, longest causal walk first: tile x, and with
   // pairing also tile ntile-1-x
+  int wx, bh;
+  wg_coords(wx, bh);
   for (int rep = 0; rep < 1 + pair; ++rep) {
-  const int tile = rep == 0 ? (int)blockIdx.x : ntile - 1 - (int)blockIdx.x;
-  if (rep == 1 && tile <= (int)blockIdx.x) break;  // odd count: the middle tile is alone
+  const int tile = rep == 0 ? wx : ntile - 1 - wx;
+  if (rep == 1 && tile <= wx) break;  // odd count: the middle tile is alone
   if (rep == 1) lds_barrier();  // the previous tile's combine has read the LDS
   const int k0 = tile * 32 * OWN;
   const int kw0 = k0 + own * 32, kj = kw0 + l32;
-  const int bh = blockIdx.y, b = bh / nh, h = bh % nh;
+  const int b = bh / nh, h = bh % nh;
   const int a = nh * D, ld = 3 * a;
   const bf16_t *Qp = qkv + (int64_t)b * s * ld + h * D;
   const bf16_t *Kp = Qp + a, *Vp = Qp + 2 * a;
@@ -515,20 +587,21 @@ __global__ void __launch_bounds__(64 * NW)
   DkdvStager<D, OWN> stg;
   stg.init(wave, lane, ld, a);
 
-  bf16x8 kf[D / 16], vf[D / 16];
-  {
-    const int krow = min(kj, s - 1);
+  // K and V of the OWN key tiles above the ring, fragment-major: 1-KB unit
+  // (own*2 + [K, V]) * D/16 + kk holds, at lane l, the 16 bytes of row l%32,
+  // columns 16 kk + 8 (l/32) .. +8 (the lane's MFMA fragment kk), so a
+  // fragment read is one base address plus an immediate offset.  Rows past
+  // the sequence read the last row (their results are masked).  The walk's
+  // first wait and barrier also cover this DMA: it is issued first.
+  constexpr int KFR = D / 16;  // fragments (1-KB units) per K or V tile
+  const uint32_t kv_lds = lds_addr(smem) + C::KV_OFF;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = load_frag(Kp + (int64_t)krow * ld + kk * 16 + hl * 8);
-      vf[kk] = load_frag(Vp + (int64_t)krow * ld + kk * 16 + hl * 8);
-    }
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      settle(kf[kk]);
-      settle(vf[kk]);
-    }
+  for (int j = 0; j < C::KVU; ++j) {
+    const int unit = j * NW + wave, blk = unit / KFR, kk = unit % KFR;
+    const int row = min(k0 + (blk >> 1) * 32 + l32, s - 1);
+    dma16_v(((blk & 1) ? Vp : Kp) + (int64_t)row * ld + kk * 16 + hl * 8, kv_lds + unit * 1024);
   }
+  const uint32_t kva = kv_lds + own * 2 * KFR * 1024 + lane * 16;  // K fragment kk at + kk KB, V after K
   f32x16 dv[D / 32], dk[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
@@ -549,16 +622,27 @@ __global__ void __launch_bounds__(64 * NW)
     const int qb = qb0 + st * SPLIT + sp, qs0 = qb * RB;
     if (qb >= nqb || (causal && qs0 + 31 < kw0)) return;
     const char *blk = smem + slot * C::STAGE_BYTES + sp * C::BLOCK_BYTES;
-    const bf16_t *qs = reinterpret_cast<const bf16_t *>(blk);
-    const bf16_t *dos = qs + B::ELEMS;
+    const uint32_t blk_lds = smem_lds + slot * C::STAGE_BYTES + sp * C::BLOCK_BYTES;
+    const uint32_t qa = B::frag_base(blk_lds, l32, hl);  // dO: + B::BYTES
+    const uint32_t qta = B::frag_t_base(blk_lds, hl);     // dO: + B::BYTES
     const float *ls = reinterpret_cast<const float *>(blk + 2 * B::BYTES);  // lse [32], delta [32]
     f32x16 sc, dp;
     zero(sc);
     zero(dp);
+    // fragments of substep kk+1 are read while the MFMAs of kk run
+    bf16x8 fr[2][4];  // [buffer][Q, K, dO, V]
+    auto read4 = [&](int kk, int buf) {
+      fr[buf][0] = B::frag_at(qa, kk);
+      fr[buf][1] = lds_frag(kva + kk * 1024);
+      fr[buf][2] = B::frag_at(qa + B::BYTES, kk);
+      fr[buf][3] = lds_frag(kva + (KFR + kk) * 1024);
+    };
+    read4(0, 0);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      sc = mfma32(B::frag(qs, l32, kk, hl), kf[kk], sc);   // S[q][key]
-      dp = mfma32(B::frag(dos, l32, kk, hl), vf[kk], dp);  // dP[q][key]
+      if (kk + 1 < D / 16) read4(kk + 1, (kk + 1) & 1);
+      sc = mfma32(fr[kk & 1][0], fr[kk & 1][1], sc);  // S[q][key]
+      dp = mfma32(fr[kk & 1][2], fr[kk & 1][3], dp);  // dP[q][key]
     }
     // masked: queries past the sequence, keys after the query (causal), and
     // keys past the sequence (lanes of a partial last key tile compute on a
@@ -605,11 +689,20 @@ __global__ void __launch_bounds__(64 * NW)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const bf16x8 pf = acc_to_frag(sc, hh), dsf = acc_to_frag(dp, hh);
+      // all transposed fragments of this half first, then its MFMAs
+      bf16x8 fo[D / 32], fq[D / 32];
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
-        dv[t] = mfma32(B::frag_t(dos, t * 32 + l32, hh * 16, hl), pf, dv[t]);
-        dk[t] = mfma32(B::frag_t(qs, t * 32 + l32, hh * 16, hl), dsf, dk[t]);
+        fo[t] = B::frag_t_at(qta + B::BYTES, t, hh);
+        fq[t] = B::frag_t_at(qta, t, hh);
       }
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        dv[t] = mfma32(fo[t], pf, dv[t]);
+        dk[t] = mfma32(fq[t], dsf, dk[t]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * (D / 32), 0);  // the transposed reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 32), 0);      // then the MFMAs
     }
   };
   walk<C::STAGES, DL>(nst, issue, compute);
@@ -689,7 +782,9 @@ __global__ void __launch_bounds__(64 * NW)
   const int l32 = lane & 31, hl = lane >> 5;
   const int own = wave % OWN, sp = wave / OWN;
   const int ntile = (s + 32 * OWN - 1) / (32 * OWN);
-  const int bh = blockIdx.y, b = bh / nh, h = bh % nh;
+  int wx, bh;
+  wg_coords(wx, bh);
+  const int b = bh / nh, h = bh % nh;
   const int a = nh * D, ld = 3 * a;
   const bf16_t *Kp = qkv + (int64_t)b * s * ld + a + h * D;
   const bf16_t *dsb = dsm + (int64_t)bh * s_pad * s_pad;
@@ -724,8 +819,8 @@ __global__ void __launch_bounds__(64 * NW)
 
   // tiles as in the forward: ntile-1-x, and with pairing also x
   for (int rep = 0; rep < 1 + pair; ++rep) {
-  const int tile = rep == 0 ? ntile - 1 - (int)blockIdx.x : (int)blockIdx.x;
-  if (rep == 1 && tile >= ntile - 1 - (int)blockIdx.x) break;
+  const int tile = rep == 0 ? ntile - 1 - wx : wx;
+  if (rep == 1 && tile >= ntile - 1 - wx) break;
   if (rep == 1) lds_barrier();  // the previous tile's combine has read the LDS
   const int q0 = tile * 32 * OWN;
   const int qw0 = q0 + own * 32;
