@@ -450,6 +450,80 @@ def study_density(names, reps=20):
     return {"study": "batch_split_density", "reps": reps, "blocks": res}
 
 
+def _graph_us(torch, s, launch, reps=20, trials=3):
+    """Best over ``trials`` of the average time of one launch in a hipGraph of
+    ``reps`` back-to-back launches on stream ``s``."""
+    with torch.cuda.stream(s):
+        launch()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(reps):
+            launch()
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / reps * 1e3)
+    del g
+    return best
+
+
+def study_libgemm(cfg):
+    """Context for the GEMM rooflines: each distinct GEMM shape of the step
+    (one sub-batch, automatic tiles, plain store: bf16 C, float32 C for the
+    weight gradients) against the vendor library on the same operands and
+    layouts (torch's matmul, which calls hipBLASLt; it writes bf16 C in all
+    cases), both as hipGraph replays.  The per-step totals weight each shape
+    by its launches in one step (the column GEMM runs in F and in R)."""
+    import torch
+    from tensor_model_transformer_tmp_amd import shard
+
+    dev = torch.device("cuda:0")
+    shapes = {}
+    for l in range(cfg.n_layers):
+        for gname, la, lb, M, N, K in _layer_gemms(cfg, l, cfg.t_sb):
+            key = (gname, la, lb, M, N, K)
+            shapes[key] = shapes.get(key, 0) + 2 * (2 if gname == "col_fwd" else 1)  # two sub-batches
+    rows, tot_ours, tot_lib = [], 0.0, 0.0
+    for (gname, la, lb, M, N, K), launches in shapes.items():
+        a = torch.randn(K * M, device=dev).to(torch.bfloat16).view((M, K) if la == 0 else (K, M))
+        b = (torch.randn(K * N, device=dev) * 0.05).to(torch.bfloat16).view((N, K) if lb == 0 else (K, N))
+        c = torch.empty(M, N, device=dev, dtype=torch.float32 if la == 1 else torch.bfloat16)
+        epi = "f32" if la == 1 else "store"
+        s = torch.cuda.Stream(device=dev)
+        ours = _graph_us(torch, s, lambda: shard.gemm(shard.BF16, a, b, c, la, lb, epi, m=M, n=N, k=K, stream=s))
+        ref = c.float().clone()
+        if la == 0 and lb == 0:
+            lib = lambda: torch.nn.functional.linear(a, b)
+        elif la == 0:
+            lib = lambda: torch.mm(a, b)
+        else:
+            at = a.t()
+            lib = lambda: torch.mm(at, b)
+        lib_us = _graph_us(torch, s, lib)
+        with torch.cuda.stream(s):
+            r = lib().float()
+        torch.cuda.synchronize()
+        diff = ((r - ref).abs().max() / r.abs().max()).item()
+        f = gemm_flops(M, N, K)
+        rows.append({"gemm": gname, "shape": [M, N, K], "layouts": [la, lb], "launches_per_step": launches,
+                     "ours_us": ours, "ours_tflops": f / ours / 1e6, "lib_us": lib_us,
+                     "lib_tflops": f / lib_us / 1e6, "ours_over_lib_time": ours / lib_us,
+                     "max_rel_diff": diff})
+        tot_ours += launches * ours
+        tot_lib += launches * lib_us
+        del a, b, c, ref, r
+    return {"study": "libgemm", "workload": cfg.name, "gemms": rows, "step_gemm_us_ours": tot_ours,
+            "step_gemm_us_lib": tot_lib, "ours_over_lib_time": tot_ours / tot_lib}
+
+
 def _preset(name):
     return gen.PRESETS[name] if name in gen.PRESETS else gen.FULL_PRESETS[name]
 
@@ -465,12 +539,13 @@ def main():
                     help="kernel class for the roofline entry (default: most time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES three times (counter calibration)")
-    ap.add_argument("--study", choices=("ablation", "density", "trace", "peaks", "kloop"), default=None,
+    ap.add_argument("--study", choices=("ablation", "density", "trace", "peaks", "kloop", "libgemm"), default=None,
                     help="run a study instead of the timed step: schedule ablation on --config, "
                          "the batch-split GEMM density study over the bf16 workloads, or "
                          "--steps eager steps of --schedule alone (for a kernel trace), or the "
                          "measured MFMA and HBM rooflines (MFMA probe; copies and sums beyond the "
-                         "Infinity Cache), or the fixed and per-k cost of a 1024-hidden GEMM")
+                         "Infinity Cache), or the fixed and per-k cost of a 1024-hidden GEMM, or "
+                         "the step's GEMM shapes of --config against the vendor library")
     ap.add_argument("--schedule", default="overlap_streams",
                     choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
                     help="schedule of the timed steps and of --study trace (default: one stream per "
@@ -497,6 +572,9 @@ def main():
         return 0
     if args.study == "kloop":
         print(json.dumps(study_kloop()), flush=True)
+        return 0
+    if args.study == "libgemm":
+        print(json.dumps(study_libgemm(_preset(args.config))), flush=True)
         return 0
     if args.study == "peaks":
         print(json.dumps(study_peaks()), flush=True)
