@@ -324,15 +324,18 @@ int oases_sum_variant(int32_t variant);
  * rows each; OWN of them own distinct row tiles (sharing each staged block)
  * and 4/OWN split the walk over the other operand.  With tile pairs a
  * workgroup takes two row tiles, one with a long and one with a short causal
- * walk.  0 = automatic (the default: for the forward, 8-wave workgroups
- * with the largest OWN in {4, 2} (or 1 for d = 64) that gives 256
- * workgroups, else the largest OWN of 4 waves that does; for the backward,
+ * walk.  0 = automatic (the default: for the causal forward with d = 128,
+ * variant 9 when it gives at least 128 workgroups; otherwise for the
+ * forward 8-wave workgroups with the largest OWN in {4, 2} (or 1 for
+ * d = 64) that gives 256 workgroups, else the largest OWN of 4 waves that
+ * does; for the backward,
  * OWN 1 with pairs when pairs alone give 256 workgroups of a causal
  * attention, else as the 4-wave forward), 1 = OWN 1, 2 = OWN 4, 3 = OWN 2,
  * 4 = OWN 1 with pairs, 5 = OWN 2 with pairs; 6, 7, 8: the forward with
  * 8-wave workgroups and OWN 2, 4, 1 (OWN 1 for d = 64 only; d = 128 runs
- * OWN 2), the backward automatic.  For tests and tuning; OASES_E_ARG for
- * other values. */
+ * OWN 2), 9: the forward with 8-wave workgroups whose two owned tiles are a
+ * long and a short causal walk; for 6 to 9 the backward is automatic.  For
+ * tests and tuning; OASES_E_ARG for other values. */
 int oases_attention_variant(int32_t variant);
 
 /* Causal (causal = 1) or full attention forward over QKV [nb*s, 3a]

@@ -343,8 +343,16 @@ __global__ void __launch_bounds__(64 * W)
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int own = wave % OWN, sp = wave / OWN;
+  // pair == 2 (OWN == 2): the two owned 32-row tiles are the heavy tile
+  // nt32-1-x and the light tile x of a causal walk, so every workgroup
+  // carries the same work; waves 0..SPLIT-1 take the heavy tile and the
+  // rest the light one, so that (waves being placed on the SIMDs in turn)
+  // each SIMD runs one wave of each.  The light tile's keys are a prefix of
+  // the heavy tile's, so both share every staged block.
+  const bool hl_pair = OWN == 2 && pair == 2;
+  const int own = hl_pair ? wave / SPLIT : wave % OWN, sp = hl_pair ? wave % SPLIT : wave / OWN;
   const int ntile = (s + 32 * OWN - 1) / (32 * OWN);
+  const int nt32 = (s + 31) / 32;
   int wx, bh;
   wg_coords(wx, bh);
   const int b = bh / nh, h = bh % nh;
@@ -357,12 +365,17 @@ __global__ void __launch_bounds__(64 * W)
 
   // tiles of this workgroup, heaviest causal walk first: tile ntile-1-x, and
   // with pairing also tile x (equal work per workgroup)
-  for (int rep = 0; rep < 1 + pair; ++rep) {
+  for (int rep = 0; rep < 1 + (pair == 1); ++rep) {
   const int tile = rep == 0 ? ntile - 1 - wx : wx;
   if (rep == 1 && tile >= ntile - 1 - wx) break;  // odd count: the middle tile is alone
   if (rep == 1) lds_barrier();  // the previous tile's combine has read the LDS
-  const int q0 = tile * 32 * OWN;
-  const int qw0 = q0 + own * 32, qi = qw0 + l32;
+  // first row of owned tile ow; with hl_pair a light tile equal to the heavy
+  // one (the middle of an odd count) is left to the heavy waves
+  const int heavy = nt32 - 1 - wx, light = wx;
+  auto row0_of = [&](int ow) { return hl_pair ? (ow == 0 ? heavy : light) * 32 : tile * 32 * OWN + ow * 32; };
+  const bool idle = hl_pair && own == 1 && light >= heavy;
+  const int q0 = hl_pair ? heavy * 32 : tile * 32 * OWN;  // the heavy (last) rows of the workgroup
+  const int qw0 = row0_of(own), qi = qw0 + l32;
 
   bf16x8 qf[D / 16];
   {
@@ -378,7 +391,7 @@ __global__ void __launch_bounds__(64 * W)
   float m_run = -INFINITY, l_run = 0.f;  // m_run: reference maximum of the raw scores
   const float slack = 8.f / scale_log2;
 
-  const int kend = causal ? min(s, q0 + 32 * OWN) : s;
+  const int kend = causal ? min(s, hl_pair ? q0 + 32 : q0 + 32 * OWN) : s;
   const int nkb = (kend + RB - 1) / RB;
   const int nst = (nkb + SPLIT - 1) / SPLIT;
 
@@ -386,7 +399,7 @@ __global__ void __launch_bounds__(64 * W)
   auto issue = [&](int st, int slot) { stg.issue(Kp, ld, s, st * SPLIT * RB, smem_lds + slot * C::STAGE_BYTES); };
   auto compute = [&](int st, int slot) {
     const int kb = st * SPLIT + sp, k0 = kb * RB;
-    if (kb >= nkb || (causal && k0 > qw0 + 31)) return;
+    if (idle || kb >= nkb || (causal && k0 > qw0 + 31)) return;
     const bf16_t *ks = reinterpret_cast<const bf16_t *>(smem + slot * C::STAGE_BYTES + sp * 2 * B::BYTES);
     const bf16_t *vs = ks + B::ELEMS;
     f32x16 sc;
@@ -447,8 +460,8 @@ __global__ void __launch_bounds__(64 * W)
   lds_barrier();
   for (int c = threadIdx.x; c < OWN * 32 * (D / 8); c += 64 * W) {
     const int q = c % 32, d0 = ((c / 32) % (D / 8)) * 8, ow = c / (32 * (D / 8));
-    const int qq = q0 + ow * 32 + q;
-    if (qq >= s) continue;
+    const int qq = row0_of(ow) + q;
+    if (qq >= s || (hl_pair && ow == 1 && light >= heavy)) continue;
     float m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < SPLIT; ++w) m = fmaxf(m, ml[((w * OWN + ow) * 2) * 32 + q]);
@@ -881,11 +894,13 @@ __global__ void __launch_bounds__(64 * NW)
 // host side
 // ---------------------------------------------------------------------------
 int g_attn_variant = 0;  // 0 automatic; 1, 2, 3: OWN = 1, 4, 2; 4, 5: OWN = 1, 2 with tile pairs;
-                         // 6, 7, 8: forward with 8 waves, OWN = 2, 4, 1
+                         // 6, 7, 8: forward with 8 waves, OWN = 2, 4, 1; 9: forward with 8 waves,
+                         // a heavy and a light tile per workgroup
 
 struct AttnPlan {
   int own;
-  int pair;   // 1: a workgroup takes two tiles, one of the longest and one of the shortest causal walks
+  int pair;   // 1: a workgroup takes two tiles, one of the longest and one of the shortest causal walks,
+              // one after the other; 2 (forward, OWN 2): its two owned tiles are such a pair
   int waves;  // waves per workgroup (the forward also runs 8)
 };
 
@@ -894,9 +909,11 @@ struct AttnPlan {
 // walks grow with the tile index; for the backward kernels, when
 // single-owner tiles paired heavy-with-light still give 256 workgroups,
 // every workgroup takes a pair (equal work per workgroup instead of a
-// longest walk twice the average).  The forward keeps shared staging (OWN 2)
-// instead: measured on MI355X, pairs help the backward by up to a fifth at
-// s = 2048 and slow the forward.
+// longest walk twice the average); measured on MI355X, pairs help the
+// backward by up to a fifth at s = 2048.  The causal forward with d = 128
+// pairs within the workgroup instead: its two owned tiles are a heavy and a
+// light one, sharing the staged blocks (one tile after the other measured
+// slower there).
 AttnPlan pick_plan(int s, int nbh, int causal, bool bwd, int d = 128) {
   switch (g_attn_variant) {
     case 1: return {1, 0, NW};
@@ -907,9 +924,13 @@ AttnPlan pick_plan(int s, int nbh, int causal, bool bwd, int d = 128) {
     case 6: if (!bwd) return {2, 0, 8}; break;
     case 7: if (!bwd) return {4, 0, 8}; break;
     case 8: if (!bwd) return {d == 64 ? 1 : 2, 0, 8}; break;  // 8 waves of one tile: d = 64 only (LDS)
+    case 9: if (!bwd) return {2, 2, 8}; break;  // 8 waves, a heavy and a light causal tile
     default: break;
   }
   if (bwd && causal && (int64_t)((s + 31) / 32 / 2) * nbh >= 256) return {1, 1, NW};
+  if (!bwd && causal && d == 128 && (int64_t)((s + 63) / 64) * nbh >= 128)
+    return {2, 2, 8};  // a heavy and a light tile per 8-wave workgroup (measured: 11-17% faster
+                       // at s = 1024-2048 than single-tile splits, also at 128 workgroups)
   if (!bwd) {
     // forward: 8-wave workgroups (two waves per SIMD; the walk split four
     // or eight ways) when they alone give 256 workgroups
@@ -932,7 +953,7 @@ template <int D, int OWN, int W = NW>
 hipError_t fwd_launch(int nb, int s, int nh, int causal, int pair, const void *qkv, void *o, float *lse,
                       hipStream_t st) {
   const float scale = 1.f / sqrtf((float)D);
-  const dim3 grid(tile_wgs(s, OWN, pair), nb * nh);
+  const dim3 grid(tile_wgs(s, OWN, pair == 1), nb * nh);  // pair 2: one workgroup per OWN tiles
   OASES_LAUNCH((attn_fwd_kernel<D, OWN, W>), grid, dim3(64 * W), st, static_cast<const bf16_t *>(qkv),
                static_cast<bf16_t *>(o), lse, s, attn_lse_stride(s), nh, causal, scale * LOG2E, scale, pair);
   return hipSuccess;
@@ -963,7 +984,7 @@ hipError_t fwd_d(int nb, int s, int nh, int causal, const void *qkv, void *o, fl
   if (pl.waves == 8) {
     switch (pl.own) {
       case 4: return fwd_launch<D, 4, 8>(nb, s, nh, causal, 0, qkv, o, lse, st);
-      case 2: return fwd_launch<D, 2, 8>(nb, s, nh, causal, 0, qkv, o, lse, st);
+      case 2: return fwd_launch<D, 2, 8>(nb, s, nh, causal, pl.pair, qkv, o, lse, st);
       default:
         if constexpr (D == 64) return fwd_launch<D, 1, 8>(nb, s, nh, causal, 0, qkv, o, lse, st);
         return fwd_launch<D, 2, 8>(nb, s, nh, causal, 0, qkv, o, lse, st);

@@ -984,7 +984,7 @@ int oases_sum_variant(int32_t variant) {
 }
 
 int oases_attention_variant(int32_t variant) {
-  if (variant < 0 || variant > 8) return OASES_E_ARG;
+  if (variant < 0 || variant > 9) return OASES_E_ARG;
   attention_set_variant(variant);
   return OASES_OK;
 }

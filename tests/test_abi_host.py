@@ -157,7 +157,7 @@ def test_single_kernel_entry_validation():
     assert L.oases_gemm(1, 0, 0, 0, 0, 16, 16, 16, 16, 32, 16, 48, 16, None, None, None, 0, 0,
                         None) == shard.OK
     assert L.oases_gemm_tile_variant(23) == shard.E_ARG
-    assert L.oases_attention_variant(9) == shard.E_ARG
+    assert L.oases_attention_variant(10) == shard.E_ARG
     assert L.oases_attention_variant(-1) == shard.E_ARG
     assert L.oases_attention_fwd(1, 8, 1, 96, 1, 16, 32, 48, None) == shard.E_ARG
 

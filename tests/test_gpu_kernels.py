@@ -90,7 +90,7 @@ def test_gemm_fwd_f32():
     assert_close(c.cpu().numpy(), blocks.gelu(ref), 1e-6, "gelu")
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("nb,s,nh,causal", [(1, 1, 1, True), (2, 100, 3, True), (1, 300, 2, False),
                                             (2, 512, 2, True), (1, 1030, 1, True)])

@@ -141,7 +141,7 @@ def test_layer_entry_points_match_schedule_step():
     dev.close()
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 9])
 @pytest.mark.parametrize("name", ["pair_d64_ragged", "pair_d128"])
 def test_attention_variants_full_step(variant, name):
     """Every attention work split (1, 2 or 4 owner waves; single tiles or
