@@ -166,7 +166,7 @@ int main() {
   EXPECT(oases_allreduce_point(OASES_BF16, fake(0), fake(1), 8, 1, fake(2), 12, nullptr) == OASES_E_ARG);
   EXPECT(oases_mfma_probe(0, 1, nullptr, nullptr) == OASES_E_ARG);
   EXPECT(oases_gemm_tile_variant(23) == OASES_E_ARG);
-  EXPECT(oases_attention_variant(9) == OASES_E_ARG);
+  EXPECT(oases_attention_variant(10) == OASES_E_ARG);
   EXPECT(oases_sum_grid_cap(0) == OASES_E_ARG);
   EXPECT(oases_sum_variant(3) == OASES_E_ARG);
   EXPECT(oases_sum_variant(-1) == OASES_E_ARG);
