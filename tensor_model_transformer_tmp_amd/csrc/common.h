@@ -152,26 +152,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Transpose an 8x8 block of bf16 held as 8 rows of uint4 (row i = r[i], 8
-// elements each) into 8 columns: o[j] holds element j of r[0..7].
-__device__ __forceinline__ void transpose8x8_bf16(const uint4 (&r)[8], uint4 (&o)[8]) {
-  const uint32_t *rw[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) rw[i] = reinterpret_cast<const uint32_t *>(&r[i]);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t a = rw[2 * p][j >> 1], b = rw[2 * p + 1][j >> 1];
-      // even j: low halves of a and b; odd j: high halves
-      w[p] = (j & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                     : __builtin_amdgcn_perm(b, a, 0x05040100u);
-    }
-    o[j] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // GeLU and its derivative in float32, gelu(u) = u * Phi(u) with the standard
 // normal CDF Phi(u) = (1 + erf(u / sqrt 2)) / 2.  erf is evaluated with the
 // rational-exponential approximation 7.1.26 of Abramowitz & Stegun (Handbook

@@ -7,19 +7,19 @@
 //   data gradient         dX[T, K] = dC[T, N] W[N, K]         (A KC, B MC)
 //   weight gradient       dW[N, K] = dC[T, N]^T X[T, K]       (A MC, B MC)
 //
-// Tiling: a workgroup of 4 waves (2 x 2) computes a BM x BN tile of C.  Each
-// operand tile is held in LDS as [rows][64] bf16, k contiguous, with the
-// 16-byte chunks of row r XOR-swizzled by ((r ^ (r >> 3)) & 7) so that the
-// 16-byte fragment reads of 16 consecutive rows hit distinct banks of the
-// 64-bank LDS (measured: no bank-conflict cycles).
-//   * k-contiguous operands (KC) with K a multiple of 64 are copied HBM -> LDS
-//     by the gfx950 LDS DMA (global_load_lds_dwordx4), STAGES-1 tiles ahead,
-//     without passing through registers.
-//   * other operands go through registers: m/n-contiguous ones (MC) are read
-//     as 8x8 bf16 blocks and transposed in registers on their way into LDS.
+// Tiling: a workgroup of WGM x WGN waves (4 or 8) computes a BM x BN tile of
+// C; the tile shape is chosen per problem (dispatch_tile).  Every operand
+// tile goes HBM -> LDS by the gfx950 LDS DMA (global_load_lds_dwordx4),
+// STAGES-1 k tiles ahead, without passing through registers.
+//   * k-contiguous operands (KC) are held as [rows][BK] bf16 with the 16-byte
+//     chunks of row r XOR-swizzled (kc_key), so that the 16-byte fragment
+//     reads of 16 consecutive rows hit distinct banks of the 64-bank LDS
+//     (measured: no bank-conflict cycles).
+//   * m/n-contiguous operands (MC) are stored as they are and read with the
+//     gfx950 transposing LDS read (McTile).
 // The MFMA computes the transposed tile C^T = B^T A^T, so a lane owns one row
-// m of C and runs of four consecutive columns n, which the epilogue writes as
-// 8- or 16-byte vectors.
+// m of C and runs of four consecutive columns n; the epilogue writes them as
+// 16-byte vectors.
 #include <type_traits>
 
 #include "common.h"
