@@ -628,10 +628,14 @@ def main():
     # dominate 5-20 us ones (the 1024-hidden pair): their step time is
     # reported, and the timeline figures are withheld where it exceeds the
     # timed steps' by more than 15%.
-    cap = min(1 << 16, sum(class_launches(cfg, kc) for kc in KERNEL_CLASSES) * args.steps + 64)
+    # the instrumented block records at most 65536 launches: long runs
+    # instrument their first n_inst steps
+    per_step_launches = sum(class_launches(cfg, kc) for kc in KERNEL_CLASSES)
+    n_inst = min(args.steps, ((1 << 16) - 64) // per_step_launches)
+    cap = per_step_launches * n_inst + 64
     wall, per_step = steps_with_events(args.steps, use_graph)
     dev.ctx.profile_begin("all", cap)
-    _, instrumented = steps_with_events(args.steps, False)
+    _, instrumented = steps_with_events(n_inst, False)
     tl = dev.ctx.profile_timeline(cap)
     # each kernel class alone: a few steps of the serial schedule (same
     # kernels, one stream, nothing running beside a launch), events as above
@@ -646,14 +650,14 @@ def main():
     solo = {}
     for cls, _, a, b in tl_solo:
         solo.setdefault(cls, []).append((b - a) * 1e3)  # us
-    fig, _ = overlap_report(rows, args.steps)
+    fig, _ = overlap_report(rows, n_inst)
     ms_step = median(per_step)
     trusted = median(instrumented) <= 1.15 * ms_step
     f, r, b = step_flops(cfg)
     flops = f + r + b
     value = flops / (ms_step / 1e3) / 1e12
 
-    n_steps = args.steps
+    n_steps = n_inst
     kernels = {}
     for kc in KERNEL_CLASSES:
         work, unit = class_work(cfg, kc)
@@ -708,7 +712,7 @@ def main():
                       if cfg.full_block else {})},
         "timing": "median of per-step HIP-event times on the compute stream over the timed steps",
         "wall_ms_per_step": wall / args.steps * 1e3,
-        "instrumented_ms_per_step": median(instrumented),
+        "instrumented_ms_per_step": median(instrumented), "instrumented_steps": n_inst,
         "instrumented_over_timed": median(instrumented) / ms_step,
         "mfma_peak_frac": value / (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == gen.BF16 else FP32_PEAK_TFLOPS),
         # the part of the AllReduce-point sums' time during which a GEMM or

@@ -106,11 +106,6 @@ __device__ __forceinline__ void wg_coords(int &x, int &bh) {
   bh = lin % nbh;
   x = lin / nbh;
 }
-// 16 bytes of LDS at a 32-bit LDS byte address
-__device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr);
-}
 
 // Make the compiler wait for (and keep) values loaded from global memory
 // before the walk starts.  The LDS DMA is invisible to the compiler's wait

@@ -126,6 +126,12 @@ __device__ __forceinline__ void dma16_v(const void *src, uint32_t lds) {
                : "m0", "memory");
 }
 
+// 16 bytes of LDS at a 32-bit LDS byte address
+__device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr);
+}
+
 // Chunk swizzle of a row-major bf16 tile read with ds_read_b64_tr_b16: a read
 // covers 4 consecutive rows x 64 bytes per 32 lanes.  16-byte chunk c of row
 // k is stored at c ^ mc_swz(k) so those rows land in distinct 64-byte

@@ -10,7 +10,10 @@
 // Tiling: a workgroup of WGM x WGN waves (4 or 8) computes a BM x BN tile of
 // C; the tile shape is chosen per problem (dispatch_tile).  Every operand
 // tile goes HBM -> LDS by the gfx950 LDS DMA (global_load_lds_dwordx4),
-// STAGES-1 k tiles ahead, without passing through registers.
+// without passing through registers, into a ring of STAGES slots.  The k
+// loop is software-pipelined: the barrier of each k tile, its first LDS
+// reads and the DMA refilling the slot just consumed all sit under the
+// previous tile's last MFMAs.
 //   * k-contiguous operands (KC) are held as [rows][BK] bf16 with the 16-byte
 //     chunks of row r XOR-swizzled (kc_key), so that the 16-byte fragment
 //     reads of 16 consecutive rows hit distinct banks of the 64-bank LDS
@@ -90,9 +93,26 @@ struct KcTile {
       }
     }
   }
-  // MFMA fragment: 8 consecutive k (half hl of substep ks) of tile row `row`
-  __device__ __forceinline__ static bf16x8 frag(const bf16_t *tile, int row, int ks, int hl) {
-    return *reinterpret_cast<const bf16x8 *>(tile + row * BK + (((ks * 2 + hl) ^ kc_key<BK>(row)) << 3));
+  __device__ __forceinline__ static const bf16_t *tile_base(const bf16_t *p, int ld, int row0, int k0) {
+    return p + (int64_t)row0 * ld + k0;
+  }
+  // unit j of a full k tile whose origin is `base`
+  __device__ __forceinline__ void issue_unit(const bf16_t *base, int j, uint32_t tile, int wave) const {
+    dma16_s(base, voff[j], tile + (j * NW + wave) * 1024);
+  }
+  // MFMA fragments: 8 consecutive k (half hl of substep ks) of a tile row.
+  // The chunk swizzle is an XOR, so a lane addresses all its fragments from
+  // one base, the LDS byte address of substep 0 of its first row: substep ks
+  // is the base XOR (ks << 5), and for the row 32 i further down the key
+  // changes by XOR 4 i when BK = 64 (bit 6 of the address for odd i; the key
+  // of 32-deep rows is unchanged).  Row and slot offsets are multiples of 128
+  // bytes, so they add as immediates.
+  __device__ __forceinline__ static uint32_t frag_base(uint32_t tile, int row, int hl) {
+    return tile + (uint32_t)(row * BK * 2 + ((hl ^ kc_key<BK>(row)) << 4));
+  }
+  __device__ __forceinline__ static bf16x8 frag_at(uint32_t base, int slot_off, int ks, int i) {
+    const uint32_t x = (uint32_t)((ks << 5) ^ (BK == 64 ? (i & 1) << 6 : 0));
+    return lds_frag((base ^ x) + slot_off + i * 32 * BK * 2);
   }
 };
 
@@ -133,6 +153,12 @@ struct McTile {
         dma16_v(k0 + unit_k(j * NW + wave, lane) < K ? base + voff[j] / 2 : zero_page(),
                 tile + (j * NW + wave) * 1024);
     }
+  }
+  __device__ __forceinline__ static const bf16_t *tile_base(const bf16_t *p, int ld, int col0, int k0) {
+    return p + (int64_t)k0 * ld + col0;
+  }
+  __device__ __forceinline__ void issue_unit(const bf16_t *base, int j, uint32_t tile, int wave) const {
+    dma16_s(base, voff[j], tile + (j * NW + wave) * 1024);
   }
   __device__ __forceinline__ static bf16x8 frag(const bf16_t *tile, int row, int ks, int hl) {
     // `row` is this lane's column of the operand (its m or n); the group's base is row - (lane & 15)
@@ -371,7 +397,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN * KS) gemm_bf16_kernel(GemmArgs
   using TA = Tile<BM, NW, LA, BK>;
   using TB = Tile<BN, NW, LB, BK>;
   constexpr int DL = TA::PER_WAVE + TB::PER_WAVE;  // DMA instructions per wave per stage
-  static_assert((STAGES - 2) * DL < 64, "vmcnt range");
+  static_assert((STAGES - 1) * DL < 64, "vmcnt range");
+  static_assert(BK / 16 % 2 == 0, "even substep count");
   static_assert(STAGES * KS * (BM + BN) * BK * 2 <= 160 * 1024, "LDS");
   // LDS ring of STAGES slots per operand and k group, always indexed with
   // compile-time slot numbers (fragment reads get immediate offsets from the
@@ -437,91 +464,126 @@ __global__ void __launch_bounds__(64 * WGM * WGN * KS) gemm_bf16_kernel(GemmArgs
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
-  // prologue: stages 0 .. STAGES-2 in flight
-  static_for<0, STAGES - 1>([&](auto I) {
+  // the k loop, software-pipelined across k tiles.  The fragments of
+  // substep ks+1 are read from LDS while the MFMAs of substep ks run.  In the
+  // last substep of tile kt each wave waits for its DMA of tile kt+1, passes
+  // the workgroup barrier (every wave has then also finished reading tile kt)
+  // and reads tile kt+1's first fragments; tile kt's slot is refilled with
+  // tile kt+STAGES while that substep's MFMAs run.  The LDS latency of a new
+  // tile and the barrier thus sit under MFMAs, and every slot's tile is in
+  // flight for STAGES-1 tiles.
+  constexpr int NKS = BK / 16;  // k substeps per tile
+  constexpr int MF = TM * TN;   // MFMAs per substep
+  constexpr int RD = TM * (LA == KC ? 1 : 2) + TN * (LB == KC ? 1 : 2);  // LDS reads per substep
+  const int nkf = min(nk, g.K / BK - kt0);  // this group's full k tiles
+  static_for<0, STAGES>([&](auto I) {
     if (decltype(I)::value < nk) issue(I, decltype(I)::value);
   });
-
-  // one k tile in LDS slot I (static); stage kt+STAGES-1 goes to slot I+STAGES-1
-  // (always inlined: an outlined step would keep the accumulators in scratch)
-  auto step = [&](auto I, int kt) __attribute__((always_inline)) {
-    using AHEAD = std::integral_constant<int, (decltype(I)::value + STAGES - 1) % STAGES>;
-    // this stage's DMA is done once at most the later stages' DMA is outstanding
-    wait_vmcnt_upto<STAGES - 2, DL>(min(STAGES - 2, nk - 1 - kt));
-    lds_barrier();
-    // the next stage's DMA: all at once with a 2-stage ring (one step of
-    // prefetch: it cannot wait); with deeper rings spread over the first two
-    // substeps, A's units with the first and B's with the second, so the
-    // address unit is fed between MFMAs instead of in one burst (measured on
-    // MI355X: 128x256 and 128x128 tiles 5-11% faster, 256x256 2-stage slower)
-    constexpr bool SPREAD = STAGES >= 3 && BK / 16 >= 2;
-    const bool ahead = kt + STAGES - 1 < nk;
-    if constexpr (!SPREAD)
-      if (ahead) issue(AHEAD{}, kt + STAGES - 1);
-
-    const bf16_t *a_s = slotA(I);
-    const bf16_t *b_s = slotB(I);
-    // fragments double-buffered in registers: the LDS reads of k-substep
-    // ks+1 are issued while the MFMAs of ks run
-    bf16x8 xa[2][TM], wb[2][TN];
-    auto read_frags = [&](int ks, int buf) {
+  bf16x8 xa[2][TM], wb[2][TN];
+  uint32_t fa0 = 0, fb0 = 0;  // KC fragment bases (slot 0)
+  if constexpr (LA == KC) fa0 = TA::frag_base(lds_addr(slotA(std::integral_constant<int, 0>{})), wm * WTM + l32, hl);
+  if constexpr (LB == KC) fb0 = TB::frag_base(lds_addr(slotB(std::integral_constant<int, 0>{})), wn * WTN + l32, hl);
+  auto read_frags = [&](auto I, int ks, int buf) __attribute__((always_inline)) {
+    constexpr int SI = decltype(I)::value;
 #pragma unroll
-      for (int i2 = 0; i2 < TM; ++i2) xa[buf][i2] = TA::frag(a_s, wm * WTM + i2 * 32 + l32, ks, hl);
+    for (int i2 = 0; i2 < TM; ++i2) {
+      if constexpr (LA == KC) xa[buf][i2] = TA::frag_at(fa0, SI * KS * BM * BK * 2, ks, i2);
+      else xa[buf][i2] = TA::frag(slotA(I), wm * WTM + i2 * 32 + l32, ks, hl);
+    }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) wb[buf][j] = TB::frag(b_s, wn * WTN + j * 32 + l32, ks, hl);
-    };
-    read_frags(0, 0);
-    // k substeps unrolled at compile time, so every fragment and accumulator
-    // index is a constant before the register promotion of local arrays
-    static_for<0, BK / 16>([&](auto KSUB) {
-      constexpr int ks = decltype(KSUB)::value;
-      if constexpr (SPREAD && ks == 0)
-        if (ahead) ta.issue(A, g.lda, m0, (kt0 + kt + STAGES - 1) * BK, g.K, lds_addr(slotA(AHEAD{})), wave, lane);
-      if constexpr (SPREAD && ks == 1)
-        if (ahead) tb.issue(B, g.ldb, n0, (kt0 + kt + STAGES - 1) * BK, g.K, lds_addr(slotB(AHEAD{})), wave, lane);
-      if constexpr (ks + 1 < BK / 16) read_frags(ks + 1, (ks + 1) & 1);
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (LB == KC) wb[buf][j] = TB::frag_at(fb0, SI * KS * BN * BK * 2, ks, j);
+      else wb[buf][j] = TB::frag(slotB(I), wn * WTN + j * 32 + l32, ks, hl);
+    }
+  };
+  auto mfma_one = [&](int buf, int j, int i2) __attribute__((always_inline)) {
+    acc[j][i2] = mfma32(wb[buf][j], xa[buf][i2], acc[j][i2]);
+  };
+  auto colsum = [&](int buf) __attribute__((always_inline)) {
+    if constexpr (COL) {
+      const bf16x2v one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i2 = 0; i2 < TM; ++i2) acc[j][i2] = mfma32(wb[ks & 1][j], xa[ks & 1][i2], acc[j][i2]);
-      if constexpr (COL) {
-        const bf16x2v one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int i2 = 0; i2 < TM; ++i2) {
-          const uint4 u = __builtin_bit_cast(uint4, xa[ks & 1][i2]);
-          float c = csum[i2];
-          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.x), one, c, false);
-          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.y), one, c, false);
-          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.z), one, c, false);
-          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.w), one, c, false);
-          csum[i2] = c;
-        }
+      for (int i2 = 0; i2 < TM; ++i2) {
+        const uint4 u = __builtin_bit_cast(uint4, xa[buf][i2]);
+        float c = csum[i2];
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.x), one, c, false);
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.y), one, c, false);
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.z), one, c, false);
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, u.w), one, c, false);
+        csum[i2] = c;
       }
-    });
-    // schedule: fragment reads of substep 0, then each MFMA of substep ks
-    // followed by one LDS read of substep ks+1
-    constexpr int RD = TM * (LA == KC ? 1 : 2) + TN * (LB == KC ? 1 : 2), MF = TM * TN;
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    }
+  };
+  wait_vmcnt_upto<STAGES - 1, DL>(min(STAGES - 1, nk - 1));  // tile 0 landed
+  lds_barrier();
+  read_frags(std::integral_constant<int, 0>{}, 0, 0);
+  // one k tile in slot I.  FULL: tile kt+STAGES exists and is a full k tile,
+  // so its DMA goes out a unit at a time between the last substep's MFMAs
+  auto step = [&](auto I, int kt, auto FULL) __attribute__((always_inline)) {
+    using NEXT = std::integral_constant<int, (decltype(I)::value + 1) % STAGES>;
+    static_for<0, NKS>([&](auto KSUB) {
+      constexpr int ks = decltype(KSUB)::value, cur = ks & 1;
+      if constexpr (ks + 1 < NKS) {
+        read_frags(I, ks + 1, cur ^ 1);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int t = 0; t < MF; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (ks + 1 < BK / 16) {
-          constexpr int PER = (RD + MF - 1) / MF;  // reads to place after each MFMA
+          for (int i2 = 0; i2 < TM; ++i2) mfma_one(cur, j, i2);
+        colsum(cur);
+        // each MFMA followed by its share of the next substep's reads
+        constexpr int PER = (RD + MF - 1) / MF;
+#pragma unroll
+        for (int t = 0; t < MF; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
           for (int q = 0; q < PER; ++q)
             if (t * PER + q < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+      } else if constexpr (decltype(FULL)::value) {
+        wait_vmcnt<(STAGES - 2) * DL>();  // tile kt+1 landed
+        lds_barrier();
+        read_frags(NEXT{}, 0, 0);
+        const int k0 = (kt0 + kt + STAGES) * BK;
+        const bf16_t *ba = TA::tile_base(A, g.lda, m0, k0);
+        const bf16_t *bb = TB::tile_base(B, g.ldb, n0, k0);
+        const uint32_t la = lds_addr(slotA(I)), lb = lds_addr(slotB(I));
+        static_for<0, MF>([&](auto T) {
+          constexpr int t = decltype(T)::value;
+          mfma_one(cur, t / TM, t % TM);
+          // the DL units of the tile spread evenly over the MF MFMAs
+          static_for<t * DL / MF, (t + 1) * DL / MF>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if constexpr (u < TA::PER_WAVE) ta.issue_unit(ba, u, la, wave);
+            else tb.issue_unit(bb, u - TA::PER_WAVE, lb, wave);
+          });
+        });
+        colsum(cur);
+      } else {
+        if (kt + 1 < nk) {
+          wait_vmcnt_upto<STAGES - 2, DL>(min(STAGES - 2, nk - 2 - kt));  // tile kt+1 landed
+          lds_barrier();
+          if (kt + STAGES < nk) issue(I, kt + STAGES);
+          read_frags(NEXT{}, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int i2 = 0; i2 < TM; ++i2) mfma_one(cur, j, i2);
+        colsum(cur);
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
-  // full groups of STAGES k tiles (slots 0..STAGES-1 in order), then the tail
+  // groups of STAGES k tiles (slots 0..STAGES-1 in order): first those whose
+  // refills are full tiles, then the rest, then the tail
   int kt = 0;
-  for (; kt + STAGES <= nk; kt += STAGES) static_for<0, STAGES>([&](auto I) { step(I, kt + decltype(I)::value); });
+  for (; kt + 2 * STAGES <= nkf; kt += STAGES)
+    static_for<0, STAGES>([&](auto I) { step(I, kt + decltype(I)::value, std::true_type{}); });
+  for (; kt + STAGES <= nk; kt += STAGES)
+    static_for<0, STAGES>([&](auto I) { step(I, kt + decltype(I)::value, std::false_type{}); });
   static_for<0, STAGES - 1>([&](auto I) {
-    if (kt + decltype(I)::value < nk) step(I, kt + decltype(I)::value);
+    if (kt + decltype(I)::value < nk) step(I, kt + decltype(I)::value, std::false_type{});
   });
 
   if constexpr (KS == 2) {
