@@ -272,6 +272,102 @@ def study_trace(cfg, mode, steps, warmup, timeline_out=None):
             "warmup": warmup, "ms_per_step": t * 1e3, "event_timeline": fig}
 
 
+def power_sampler(out_path, stop_path, max_s=300.0):
+    """Child process of --study power (it never touches the GPU through HIP):
+    reads the board's socket power and the graphics clocks with amd-smi in a
+    loop and appends one JSON line per reading, until the stop file appears."""
+    import re
+    import subprocess
+    t_end = time.time() + max_s
+    with open(out_path, "a") as fh:
+        while not os.path.exists(stop_path) and time.time() < t_end:
+            t = time.time()
+            try:
+                txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                                     timeout=20).stdout
+            except (OSError, subprocess.TimeoutExpired):
+                fh.write(json.dumps({"t": t, "error": "amd-smi unavailable"}) + "\n")
+                return 0
+            pw = re.search(r"SOCKET_POWER:\s*([\d.]+)\s*W", txt)
+            clk = [int(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", txt)]
+            fh.write(json.dumps({"t": t, "t_done": time.time(), "power_w": float(pw.group(1)) if pw else None,
+                                 "gfx_mhz": clk}) + "\n")
+            fh.flush()
+    return 0
+
+
+def study_power(cfg, mode, seconds, warmup):
+    """Board power and graphics clock while the timed step runs: a child
+    process samples amd-smi (socket power, current clock of every XCD) from
+    before the GPU is first used until the steps end; readings taken inside
+    the timed window (after its first second) are summarised.  The MFMA peak
+    of 2.5 PFLOP/s assumes the 2.4 GHz peak clock; the same peak at the
+    measured clock is reported beside it."""
+    import subprocess
+    import tempfile
+    from statistics import median
+    tmp = tempfile.mkdtemp(prefix="oases_power_")
+    out_path, stop_path = os.path.join(tmp, "samples.jsonl"), os.path.join(tmp, "stop")
+    # started before this process initialises the GPU
+    child = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--power-sampler", out_path, stop_path])
+    try:
+        import torch
+        from tensor_model_transformer_tmp_amd.device import DeviceShard
+
+        time.sleep(2.0)  # idle readings
+        t_gpu = time.time()
+        dev = DeviceShard(gen.make_inputs(cfg), device="cuda:0", modes=(mode,))
+        cs = dev.compute
+        for _ in range(warmup):
+            dev.ctx.schedule_step(mode, False)
+        torch.cuda.synchronize()
+        f, r, b = step_flops(cfg)
+        times, t0 = [], time.time()
+        while time.time() - t0 < seconds:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cs)
+            dev.ctx.schedule_step(mode, False)
+            e1.record(cs)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        t1 = time.time()
+        dev.close()
+    finally:
+        open(stop_path, "w").close()
+        try:
+            child.wait(timeout=60)
+        except subprocess.TimeoutExpired:
+            child.kill()
+            child.wait()
+    rows = []
+    if os.path.exists(out_path):
+        with open(out_path) as fh:
+            rows = [json.loads(x) for x in fh if x.strip()]
+    idle = [x for x in rows if x.get("t_done", 0) < t_gpu and x.get("power_w") is not None]
+    busy = [x for x in rows if x.get("t", 0) >= t0 + 1.0 and x.get("t_done", 1e30) <= t1
+            and x.get("power_w") is not None]
+    ms = median(times)
+    out = {"study": "power", "workload": cfg.name, "schedule": mode + "+eager", "seconds": seconds,
+           "steps": len(times), "ms_per_step": ms, "tflops": (f + r + b) / (ms / 1e3) / 1e12,
+           "readings_in_window": len(busy)}
+    if not busy:
+        out["note"] = "no amd-smi readings inside the timed window"
+        if rows and "error" in rows[0]:
+            out["note"] = rows[0]["error"]
+        return out
+    mhz = [sum(x["gfx_mhz"]) / len(x["gfx_mhz"]) for x in busy if x["gfx_mhz"]]
+    clk = median(mhz)
+    out.update({
+        "idle_power_w": median([x["power_w"] for x in idle]) if idle else None,
+        "power_w": {"median": median([x["power_w"] for x in busy]), "min": min(x["power_w"] for x in busy),
+                    "max": max(x["power_w"] for x in busy)},
+        "gfx_mhz": {"median": clk, "min": min(mhz), "max": max(mhz)},
+        "mfma_bf16_peak_tflops_at_clock": MFMA_BF16_PEAK_TFLOPS * clk / 2400.0,
+        "frac_of_peak_at_clock": (f + r + b) / (ms / 1e3) / 1e12 / (MFMA_BF16_PEAK_TFLOPS * clk / 2400.0),
+    })
+    return out
+
+
 def study_peaks(reps=10):
     """The two rooflines measured on this GPU.  MFMA: a probe kernel of
     back-to-back independent bf16 32x32x16 MFMAs with register operands, at
@@ -539,13 +635,18 @@ def main():
                     help="kernel class for the roofline entry (default: most time per step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES three times (counter calibration)")
-    ap.add_argument("--study", choices=("ablation", "density", "trace", "peaks", "kloop", "libgemm"), default=None,
+    ap.add_argument("--study", choices=("ablation", "density", "trace", "peaks", "kloop", "libgemm", "power"),
+                    default=None,
                     help="run a study instead of the timed step: schedule ablation on --config, "
                          "the batch-split GEMM density study over the bf16 workloads, or "
                          "--steps eager steps of --schedule alone (for a kernel trace), or the "
                          "measured MFMA and HBM rooflines (MFMA probe; copies and sums beyond the "
                          "Infinity Cache), or the fixed and per-k cost of a 1024-hidden GEMM, or "
-                         "the step's GEMM shapes of --config against the vendor library")
+                         "the step's GEMM shapes of --config against the vendor library, or the "
+                         "board power and graphics clock (amd-smi) while --schedule steps run for "
+                         "--seconds")
+    ap.add_argument("--seconds", type=float, default=5.0, help="--study power: length of the timed window")
+    ap.add_argument("--power-sampler", nargs=2, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--schedule", default="overlap_streams",
                     choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
                     help="schedule of the timed steps and of --study trace (default: one stream per "
@@ -555,6 +656,8 @@ def main():
     ap.add_argument("--timeline-out", default=None, metavar="PATH",
                     help="--study trace: write the event timeline's text chart here")
     args = ap.parse_args()
+    if args.power_sampler:
+        return power_sampler(*args.power_sampler)
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
@@ -569,6 +672,9 @@ def main():
     if args.study == "trace":
         print(json.dumps(study_trace(_preset(args.config), args.schedule, args.steps, args.warmup,
                                      args.timeline_out)), flush=True)
+        return 0
+    if args.study == "power":
+        print(json.dumps(study_power(_preset(args.config), args.schedule, args.seconds, args.warmup)), flush=True)
         return 0
     if args.study == "kloop":
         print(json.dumps(study_kloop()), flush=True)
