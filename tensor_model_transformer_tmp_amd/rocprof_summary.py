@@ -315,6 +315,46 @@ def mfma_table(path: str, work=None) -> str:
     return "\n".join(out)
 
 
+def util_table(path: str) -> str:
+    """Per class, every percentage metric of a rocprofv3 counter run (the
+    derived ``*Util`` metrics, e.g. LdsUtil = LDS busy cycles for indexed
+    accesses over active cycles, MfmaUtil), averaged over the class's
+    dispatches weighted by GRBM_GUI_ACTIVE, and every raw SQ_ counter as its
+    mean per class launch."""
+    with open(path, newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    names = _demangle(sorted({r["Kernel_Name"] for r in rows}))
+    disp = defaultdict(dict)
+    for r in rows:
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Kernel_Name"])
+        disp[key][r["Counter_Name"]] = float(r["Counter_Value"])
+    metrics = sorted({k for c in disp.values() for k in c if k.endswith("Util")})
+    raw = sorted({k for c in disp.values() for k in c if k.startswith("SQ_")})
+    wsum = defaultdict(lambda: defaultdict(float))
+    act = defaultdict(float)
+    launches = defaultdict(int)
+    for (_, kname), c in disp.items():
+        n = names[kname]
+        cls = kernel_class(n)
+        if cls is None:
+            continue
+        a = c.get("GRBM_GUI_ACTIVE", 1.0)
+        act[cls] += a
+        for m in metrics:
+            wsum[cls][m] += c.get(m, 0.0) * a
+        for m in raw:
+            wsum[cls][m] += c.get(m, 0.0)
+        if _is_lead(n, cls):
+            launches[cls] += 1
+    head = ["class", "class launches"] + [f"{m} %" for m in metrics] + [f"{m} per launch" for m in raw]
+    out = [" | ".join(head), "|".join(["---"] * len(head))]
+    for cls in sorted(launches, key=lambda c: -act[c]):
+        vals = [f"{wsum[cls][m] / act[cls]:.1f}" for m in metrics]
+        vals += [f"{wsum[cls][m] / max(launches[cls], 1):.4g}" for m in raw]
+        out.append(" | ".join([cls, str(launches[cls])] + vals))
+    return "\n".join(out)
+
+
 def _class_work_per_launch(workload: str):
     """Algorithmic FLOPs per class launch of a named workload (bench.py's counts)."""
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -345,6 +385,8 @@ def main(argv=None):
     m = sub.add_parser("mfma")
     m.add_argument("csv")
     m.add_argument("--workload", default=None)
+    u = sub.add_parser("util")
+    u.add_argument("csv")
     for name in ("traffic", "traffic-all"):
         t = sub.add_parser(name)
         if name == "traffic":
@@ -364,6 +406,9 @@ def main(argv=None):
         return 0
     if a.cmd == "timeline":
         print(timeline(a.csv, a.steps, a.warmup, a.width, a.total_steps))
+        return 0
+    if a.cmd == "util":
+        print(util_table(a.csv))
         return 0
     if a.cmd == "mfma":
         print(mfma_table(a.csv, _class_work_per_launch(a.workload) if a.workload else None))

@@ -51,3 +51,21 @@ def test_mfma_weighted_by_active_cycles(tmp_path):
     assert abs(float(line[2]) - 32.5) < 1e-9           # (10*100 + 40*300) / 400
     assert abs(float(line[3]) - 1.024) < 1e-9          # 2e6 * 512 FLOP
     assert abs(float(line[5]) - 1.0) < 1e-9
+
+
+def test_util_table_weights_and_raw_fractions(tmp_path):
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    for d, lds, mf, act, conf in ((1, 50.0, 20.0, 100.0, 512.0), (2, 80.0, 60.0, 300.0, 0.0)):
+        for name, v in (("LdsUtil", lds), ("MfmaUtil", mf), ("GRBM_GUI_ACTIVE", act),
+                        ("SQ_LDS_BANK_CONFLICT", conf), ("CU_NUM", 256.0)):
+            rows.append({"Dispatch_Id": d, "Kernel_Name": GEMM, "Counter_Name": name, "Counter_Value": v})
+    p = tmp_path / "u.csv"
+    _write(p, fields, rows)
+    out = rs.util_table(str(p)).splitlines()
+    assert out[0] == "class | class launches | LdsUtil % | MfmaUtil % | SQ_LDS_BANK_CONFLICT per launch"
+    line = [ln for ln in out if ln.startswith("gemm_fwd")][0].split(" | ")
+    assert line[1] == "2"
+    assert abs(float(line[2]) - 72.5) < 1e-9    # (50*100 + 80*300) / 400
+    assert abs(float(line[3]) - 50.0) < 1e-9    # (20*100 + 60*300) / 400
+    assert abs(float(line[4]) - 256.0) < 1e-9   # (512 + 0) / 2 launches
