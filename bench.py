@@ -296,13 +296,15 @@ def power_sampler(out_path, stop_path, max_s=300.0):
     return 0
 
 
-def study_power(cfg, mode, seconds, warmup):
-    """Board power and graphics clock while the timed step runs: a child
-    process samples amd-smi (socket power, current clock of every XCD) from
-    before the GPU is first used until the steps end; readings taken inside
-    the timed window (after its first second) are summarised.  The MFMA peak
-    of 2.5 PFLOP/s assumes the 2.4 GHz peak clock; the same peak at the
-    measured clock is reported beside it."""
+def study_power(cfg, mode, seconds, warmup, target="step"):
+    """Board power and graphics clock while the timed step runs (or, with
+    target "probe", while the MFMA probe runs back to back: the dense bf16
+    rate the chip sustains at its power limit): a child process samples
+    amd-smi (socket power, current clock of every XCD) from before the GPU is
+    first used until the work ends; readings taken inside the timed window
+    (after its first second) are summarised.  The MFMA peak of 2.5 PFLOP/s
+    assumes the 2.4 GHz peak clock; the same peak at the measured clock is
+    reported beside it."""
     import subprocess
     import tempfile
     from statistics import median
@@ -316,22 +318,50 @@ def study_power(cfg, mode, seconds, warmup):
 
         time.sleep(2.0)  # idle readings
         t_gpu = time.time()
-        dev = DeviceShard(gen.make_inputs(cfg), device="cuda:0", modes=(mode,))
-        cs = dev.compute
+        from tensor_model_transformer_tmp_amd import shard
+        cs = torch.cuda.current_stream()
+        if target == "probe":
+            wgs = 256 * 4  # 4 workgroups of 4 waves per CU, back-to-back independent MFMAs
+            buf = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
+            work = lambda: shard.mfma_probe(wgs, 5000, buf)
+            flops = work()
+            torch.cuda.synchronize()
+        elif target == "gemm":
+            # the 8192-hidden pair's FFN-out forward GEMM, 2048 x 8192 x 4096, automatic tile
+            m_, n_, k_ = 2048, 8192, 4096
+            ga = torch.randn(m_, k_, device="cuda:0").to(torch.bfloat16)
+            gw = (torch.randn(n_, k_, device="cuda:0") * 0.02).to(torch.bfloat16)
+            gc = torch.empty(m_, n_, device="cuda:0", dtype=torch.bfloat16)
+            work = lambda: shard.gemm(shard.BF16, ga, gw, gc, 0, 0, "store")
+            flops = 2.0 * m_ * n_ * k_
+        elif target == "sum":
+            # one AllReduce point of the 8192-hidden pair: own + 7 peers of 2048 x 8192 bf16
+            n_ = 2048 * 8192
+            so = torch.ones(n_, dtype=torch.bfloat16, device="cuda:0")
+            sp = torch.ones(7, n_, dtype=torch.bfloat16, device="cuda:0")
+            sy = torch.empty_like(so)
+            work = lambda: shard.allreduce_point(shard.BF16, so, sp, 7, sy)
+            flops = 9.0 * n_ * 2  # bytes moved (reported in the TFLOP/s field as TB/s)
+        else:
+            dev = DeviceShard(gen.make_inputs(cfg), device="cuda:0", modes=(mode,))
+            cs = dev.compute
+            work = lambda: dev.ctx.schedule_step(mode, False)
+            f, r, b = step_flops(cfg)
+            flops = f + r + b
         for _ in range(warmup):
-            dev.ctx.schedule_step(mode, False)
+            work()
         torch.cuda.synchronize()
-        f, r, b = step_flops(cfg)
         times, t0 = [], time.time()
         while time.time() - t0 < seconds:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(cs)
-            dev.ctx.schedule_step(mode, False)
+            work()
             e1.record(cs)
             e1.synchronize()
             times.append(e0.elapsed_time(e1))
         t1 = time.time()
-        dev.close()
+        if target == "step":
+            dev.close()
     finally:
         open(stop_path, "w").close()
         try:
@@ -347,9 +377,20 @@ def study_power(cfg, mode, seconds, warmup):
     busy = [x for x in rows if x.get("t", 0) >= t0 + 1.0 and x.get("t_done", 1e30) <= t1
             and x.get("power_w") is not None]
     ms = median(times)
-    out = {"study": "power", "workload": cfg.name, "schedule": mode + "+eager", "seconds": seconds,
-           "steps": len(times), "ms_per_step": ms, "tflops": (f + r + b) / (ms / 1e3) / 1e12,
-           "readings_in_window": len(busy)}
+    out = {"study": "power", "target": target, "seconds": seconds, "steps": len(times), "ms_per_step": ms,
+           "tflops": flops / (ms / 1e3) / 1e12, "readings_in_window": len(busy)}
+    if target == "probe":
+        out["workload"] = "mfma_probe (4 workgroups of 4 waves per CU, bf16 32x32x16)"
+    elif target == "gemm":
+        out["workload"] = "bf16 GEMM 2048 x 8192 x 4096, both operands k-contiguous"
+    elif target == "sum":
+        out["workload"] = "AllReduce-point sum, own + 7 peers of 2048 x 8192 bf16 ('tflops' is TB/s moved)"
+    else:
+        out.update({"workload": cfg.name, "schedule": mode + "+eager"})
+    if target != "step":
+        out.pop("ms_per_step")
+        out["us_per_launch"] = ms * 1e3
+        out["launches"] = out.pop("steps")
     if not busy:
         out["note"] = "no amd-smi readings inside the timed window"
         if rows and "error" in rows[0]:
@@ -363,7 +404,8 @@ def study_power(cfg, mode, seconds, warmup):
                     "max": max(x["power_w"] for x in busy)},
         "gfx_mhz": {"median": clk, "min": min(mhz), "max": max(mhz)},
         "mfma_bf16_peak_tflops_at_clock": MFMA_BF16_PEAK_TFLOPS * clk / 2400.0,
-        "frac_of_peak_at_clock": (f + r + b) / (ms / 1e3) / 1e12 / (MFMA_BF16_PEAK_TFLOPS * clk / 2400.0),
+        "frac_of_peak_at_clock": (None if target == "sum" else
+                                  flops / (ms / 1e3) / 1e12 / (MFMA_BF16_PEAK_TFLOPS * clk / 2400.0)),
     })
     return out
 
@@ -646,6 +688,9 @@ def main():
                          "board power and graphics clock (amd-smi) while --schedule steps run for "
                          "--seconds")
     ap.add_argument("--seconds", type=float, default=5.0, help="--study power: length of the timed window")
+    ap.add_argument("--power-target", default="step", choices=("step", "probe", "gemm", "sum"),
+                    help="--study power: run the timed step, or back to back the MFMA probe, the "
+                         "8192-hidden FFN-out GEMM or one of its AllReduce points")
     ap.add_argument("--power-sampler", nargs=2, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--schedule", default="overlap_streams",
                     choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
@@ -674,7 +719,8 @@ def main():
                                      args.timeline_out)), flush=True)
         return 0
     if args.study == "power":
-        print(json.dumps(study_power(_preset(args.config), args.schedule, args.seconds, args.warmup)), flush=True)
+        print(json.dumps(study_power(_preset(args.config), args.schedule, args.seconds, args.warmup,
+                                     args.power_target)), flush=True)
         return 0
     if args.study == "kloop":
         print(json.dumps(study_kloop()), flush=True)
