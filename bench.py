@@ -279,8 +279,9 @@ def power_sampler(out_path, stop_path, max_s=300.0):
     import re
     import subprocess
     t_end = time.time() + max_s
+    parent = os.getppid()
     with open(out_path, "a") as fh:
-        while not os.path.exists(stop_path) and time.time() < t_end:
+        while not os.path.exists(stop_path) and time.time() < t_end and os.getppid() == parent:
             t = time.time()
             try:
                 txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
@@ -296,6 +297,53 @@ def power_sampler(out_path, stop_path, max_s=300.0):
     return 0
 
 
+def under_profiler() -> bool:
+    """True when running under rocprofv3 (its tool library is preloaded into
+    every child process too, so no sampler child may be started then)."""
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return True
+    return any(k.startswith(("ROCPROF", "ROCP_")) for k in os.environ)
+
+
+class PowerSampler:
+    """amd-smi readings (socket power, per-XCD clock) from a child process,
+    started before this process first uses the GPU."""
+
+    def __init__(self, max_s=300.0):
+        import subprocess
+        import tempfile
+        tmp = tempfile.mkdtemp(prefix="oases_power_")
+        self.out_path, self.stop_path = os.path.join(tmp, "samples.jsonl"), os.path.join(tmp, "stop")
+        self.child = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--power-sampler",
+                                       self.out_path, self.stop_path, str(max_s)])
+
+    def stop(self):
+        import subprocess
+        open(self.stop_path, "w").close()
+        try:
+            self.child.wait(timeout=60)
+        except subprocess.TimeoutExpired:
+            self.child.kill()
+            self.child.wait()
+        rows = []
+        if os.path.exists(self.out_path):
+            with open(self.out_path) as fh:
+                rows = [json.loads(x) for x in fh if x.strip()]
+        return rows
+
+    @staticmethod
+    def summary(rows, t0, t1):
+        """Median power and clock of the readings taken inside [t0 + 1 s, t1]."""
+        from statistics import median
+        busy = [x for x in rows if x.get("t", 0) >= t0 + 1.0 and x.get("t_done", 1e30) <= t1
+                and x.get("power_w") is not None and x.get("gfx_mhz")]
+        if not busy:
+            return None
+        mhz = [sum(x["gfx_mhz"]) / len(x["gfx_mhz"]) for x in busy]
+        return {"readings": len(busy), "power_w": median([x["power_w"] for x in busy]),
+                "gfx_mhz": median(mhz), "gfx_mhz_min": min(mhz), "gfx_mhz_max": max(mhz)}
+
+
 def study_power(cfg, mode, seconds, warmup, target="step"):
     """Board power and graphics clock while the timed step runs (or, with
     target "probe", while the MFMA probe runs back to back: the dense bf16
@@ -305,13 +353,10 @@ def study_power(cfg, mode, seconds, warmup, target="step"):
     (after its first second) are summarised.  The MFMA peak of 2.5 PFLOP/s
     assumes the 2.4 GHz peak clock; the same peak at the measured clock is
     reported beside it."""
-    import subprocess
-    import tempfile
     from statistics import median
-    tmp = tempfile.mkdtemp(prefix="oases_power_")
-    out_path, stop_path = os.path.join(tmp, "samples.jsonl"), os.path.join(tmp, "stop")
-    # started before this process initialises the GPU
-    child = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--power-sampler", out_path, stop_path])
+    if under_profiler():
+        return {"study": "power", "note": "not run under a profiler (the sampler child would be profiled too)"}
+    sampler = PowerSampler()  # started before this process initialises the GPU
     try:
         import torch
         from tensor_model_transformer_tmp_amd.device import DeviceShard
@@ -363,16 +408,7 @@ def study_power(cfg, mode, seconds, warmup, target="step"):
         if target == "step":
             dev.close()
     finally:
-        open(stop_path, "w").close()
-        try:
-            child.wait(timeout=60)
-        except subprocess.TimeoutExpired:
-            child.kill()
-            child.wait()
-    rows = []
-    if os.path.exists(out_path):
-        with open(out_path) as fh:
-            rows = [json.loads(x) for x in fh if x.strip()]
+        rows = sampler.stop()
     idle = [x for x in rows if x.get("t_done", 0) < t_gpu and x.get("power_w") is not None]
     busy = [x for x in rows if x.get("t", 0) >= t0 + 1.0 and x.get("t_done", 1e30) <= t1
             and x.get("power_w") is not None]
@@ -691,7 +727,9 @@ def main():
     ap.add_argument("--power-target", default="step", choices=("step", "probe", "gemm", "sum"),
                     help="--study power: run the timed step, or back to back the MFMA probe, the "
                          "8192-hidden FFN-out GEMM or one of its AllReduce points")
-    ap.add_argument("--power-sampler", nargs=2, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--power-sampler", nargs="+", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the power and clock readings (amd-smi) after the timed steps")
     ap.add_argument("--schedule", default="overlap_streams",
                     choices=("overlap_streams", "overlap_fine", "overlap_fused", "serial_fine"),
                     help="schedule of the timed steps and of --study trace (default: one stream per "
@@ -702,7 +740,8 @@ def main():
                     help="--study trace: write the event timeline's text chart here")
     args = ap.parse_args()
     if args.power_sampler:
-        return power_sampler(*args.power_sampler)
+        a_ = args.power_sampler
+        return power_sampler(a_[0], a_[1], float(a_[2]) if len(a_) > 2 else 300.0)
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
@@ -735,6 +774,10 @@ def main():
         names = [n for n in gen.PRESET_ORDER if gen.PRESETS[n].dtype == gen.BF16]
         print(json.dumps(study_density(names)), flush=True)
         return 0
+
+    # board power and clock while the timed schedule runs (after the timed
+    # region, in a window of its own): the sampler starts before the GPU is used
+    sampler = None if (args.no_clock or under_profiler()) else PowerSampler(max_s=600.0)
 
     import torch
     from tensor_model_transformer_tmp_amd.device import DeviceShard
@@ -795,6 +838,16 @@ def main():
     dev.ctx.profile_begin("all", cap)
     steps_with_events(n_solo, False, "serial_fine")
     tl_solo = dev.ctx.profile_timeline(cap)
+    clock = None
+    if sampler is not None:
+        # 4 s of the timed schedule; amd-smi readings inside it (after its first second)
+        tc0 = time.time()
+        while time.time() - tc0 < 4.0:
+            for _ in range(10):
+                dev.ctx.schedule_step(mode, use_graph)
+            torch.cuda.synchronize()
+        tc1 = time.time()
+        clock = PowerSampler.summary(sampler.stop(), tc0, tc1)
     dev.close()
 
     # (start ns, end ns, stream, class, name)
@@ -875,6 +928,12 @@ def main():
         "kernels": kernels,
         "gflop_per_step": {"fwd": f / 1e9, "recompute": r / 1e9, "bwd": b / 1e9},
         "roofline": roof,
+        # board power and graphics clock (amd-smi) during 4 s of the timed
+        # schedule run after the timed region; the MFMA peak above assumes
+        # the 2.4 GHz peak clock
+        "clock": (None if clock is None else
+                  {**clock, "mfma_bf16_peak_tflops_at_clock": MFMA_BF16_PEAK_TFLOPS * clock["gfx_mhz"] / 2400.0,
+                   "value_frac_of_peak_at_clock": value / (MFMA_BF16_PEAK_TFLOPS * clock["gfx_mhz"] / 2400.0)}),
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(cfg),
     }
     print(json.dumps(line), flush=True)

@@ -48,3 +48,25 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_power_summary_takes_readings_inside_the_window():
+    rows = [{"t": 0.0, "t_done": 0.5, "power_w": 250.0, "gfx_mhz": [100, 100]},     # idle, before
+            {"t": 10.2, "t_done": 10.8, "power_w": 1300.0, "gfx_mhz": [1900, 1880]},  # first second: skipped
+            {"t": 11.2, "t_done": 11.8, "power_w": 1350.0, "gfx_mhz": [1850, 1870]},
+            {"t": 11.9, "t_done": 12.5, "power_w": 1370.0, "gfx_mhz": [1810, 1830]},
+            {"t": 13.7, "t_done": 14.3, "power_w": 900.0, "gfx_mhz": [2400, 2400]}]   # ends after the window
+    s = bench.PowerSampler.summary(rows, 10.0, 14.0)
+    assert s["readings"] == 2
+    assert s["power_w"] == 1360.0
+    assert s["gfx_mhz"] == 1840.0 and s["gfx_mhz_min"] == 1820.0 and s["gfx_mhz_max"] == 1860.0
+    assert bench.PowerSampler.summary(rows, 20.0, 30.0) is None
+
+
+def test_profiler_detection(monkeypatch):
+    for k in [k for k in os.environ if k.startswith(("ROCPROF", "ROCP_"))]:
+        monkeypatch.delenv(k)
+    monkeypatch.setenv("LD_PRELOAD", "")
+    assert not bench.under_profiler()
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so")
+    assert bench.under_profiler()
