@@ -344,7 +344,7 @@ class PowerSampler:
                 "gfx_mhz": median(mhz), "gfx_mhz_min": min(mhz), "gfx_mhz_max": max(mhz)}
 
 
-def study_power(cfg, mode, seconds, warmup, target="step"):
+def study_power(cfg, mode, seconds, warmup, target="step", tile_variant=0):
     """Board power and graphics clock while the timed step runs (or, with
     target "probe", while the MFMA probe runs back to back: the dense bf16
     rate the chip sustains at its power limit): a child process samples
@@ -377,6 +377,7 @@ def study_power(cfg, mode, seconds, warmup, target="step"):
             ga = torch.randn(m_, k_, device="cuda:0").to(torch.bfloat16)
             gw = (torch.randn(n_, k_, device="cuda:0") * 0.02).to(torch.bfloat16)
             gc = torch.empty(m_, n_, device="cuda:0", dtype=torch.bfloat16)
+            shard.set_gemm_tile_variant(tile_variant)
             work = lambda: shard.gemm(shard.BF16, ga, gw, gc, 0, 0, "store")
             flops = 2.0 * m_ * n_ * k_
         elif target == "sum":
@@ -419,6 +420,7 @@ def study_power(cfg, mode, seconds, warmup, target="step"):
         out["workload"] = "mfma_probe (4 workgroups of 4 waves per CU, bf16 32x32x16)"
     elif target == "gemm":
         out["workload"] = "bf16 GEMM 2048 x 8192 x 4096, both operands k-contiguous"
+        out["tile_variant"] = tile_variant
     elif target == "sum":
         out["workload"] = "AllReduce-point sum, own + 7 peers of 2048 x 8192 bf16 ('tflops' is TB/s moved)"
     else:
@@ -724,6 +726,8 @@ def main():
                          "board power and graphics clock (amd-smi) while --schedule steps run for "
                          "--seconds")
     ap.add_argument("--seconds", type=float, default=5.0, help="--study power: length of the timed window")
+    ap.add_argument("--tile-variant", type=int, default=0,
+                    help="--study power --power-target gemm: GEMM tile variant (0: automatic)")
     ap.add_argument("--power-target", default="step", choices=("step", "probe", "gemm", "sum"),
                     help="--study power: run the timed step, or back to back the MFMA probe, the "
                          "8192-hidden FFN-out GEMM or one of its AllReduce points")
@@ -759,7 +763,7 @@ def main():
         return 0
     if args.study == "power":
         print(json.dumps(study_power(_preset(args.config), args.schedule, args.seconds, args.warmup,
-                                     args.power_target)), flush=True)
+                                     args.power_target, args.tile_variant)), flush=True)
         return 0
     if args.study == "kloop":
         print(json.dumps(study_kloop()), flush=True)
