@@ -178,6 +178,37 @@ def test_gemm_layouts_and_tiles(variant, kind, m, n, k):
         shard.set_gemm_tile_variant(0)
 
 
+@pytest.mark.parametrize("variant", [0, 3, 4, 5, 14, 20])
+def test_gemm_empty_k(variant):
+    """k = 0: the product is zero, so C is the epilogue of zero -- the bias
+    (forward), zeros (data gradient), and the old float32 C (weight gradient
+    accumulating with beta) -- and no operand is read (the operand pointers
+    here are small buffers of the wrong size)."""
+    m, n = 200, 136
+    dev = "cuda"
+    shard.set_gemm_tile_variant(variant)
+    try:
+        rng = np.random.default_rng(variant)
+        wide_a = torch.zeros(1, 208, dtype=torch.bfloat16, device=dev)  # m-contiguous stride >= m
+        wide_b = torch.zeros(1, 136, dtype=torch.bfloat16, device=dev)  # n-contiguous stride >= n
+        narrow = torch.zeros(2, 8, dtype=torch.bfloat16, device=dev)    # k-contiguous stride 8 >= k
+        bias_bits = _bf16_bits(rng, (n,))
+        bias = to_device(bias_bits, gen.BF16, dev)
+        c = torch.full((m, n), float("nan"), device=dev).to(torch.bfloat16)
+        shard.gemm(shard.BF16, narrow, narrow, c, 0, 0, "bias", m=m, n=n, k=0, bias=bias)
+        dxc = torch.full((m, n), float("nan"), device=dev).to(torch.bfloat16)
+        shard.gemm(shard.BF16, narrow, wide_b, dxc, 0, 1, "store", m=m, n=n, k=0)
+        old = torch.from_numpy(rng.standard_normal((m, n)).astype(np.float32)).to(dev)
+        dwc = old.clone()
+        shard.gemm(shard.BF16, wide_a, wide_b, dwc, 1, 1, "f32", m=m, n=n, k=0, beta=1)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_storage(c), np.broadcast_to(bias_bits, (m, n)))
+        np.testing.assert_array_equal(to_storage(dxc), np.zeros((m, n), np.uint16))
+        np.testing.assert_array_equal(dwc.cpu().numpy(), old.cpu().numpy())
+    finally:
+        shard.set_gemm_tile_variant(0)
+
+
 def test_mfma_probe_runs():
     """The MFMA throughput probe issues its MFMAs (finite, nonzero per-lane
     checksums) and reports the FLOPs of its launch."""
