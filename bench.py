@@ -781,7 +781,12 @@ def main():
 
     # board power and clock while the timed schedule runs (after the timed
     # region, in a window of its own): the sampler starts before the GPU is used
-    sampler = None if (args.no_clock or under_profiler()) else PowerSampler(max_s=600.0)
+    sampler = None
+    if not (args.no_clock or under_profiler()):
+        try:
+            sampler = PowerSampler(max_s=600.0)
+        except OSError:  # no temporary directory or no interpreter to start: no readings
+            sampler = None
 
     import torch
     from tensor_model_transformer_tmp_amd.device import DeviceShard
