@@ -192,7 +192,8 @@ std::vector<Op> build_ops(int L, int mode) {
       if (mode != OASES_SERIAL_NO_RECOMPUTE) ops.push_back({OP_R, l, sb, by_sb ? sb : 0});
       if (mode == OASES_SERIAL_DEFAULT_RECOMPUTE) ops.push_back({OP_CR, l, sb, 0});
       ops.push_back({OP_BDX, l, sb, by_sb ? sb : 0});
-      ops.push_back({OP_CB, l, sb, by_sb ? sb : side});
+      // by sub-batch: the step's last C(B) runs on sub-batch 0's stream (op_CB)
+      ops.push_back({OP_CB, l, sb, by_sb ? (l == 0 ? 0 : sb) : side});
       ops.push_back({OP_BDW, l, sb, by_sb ? sb : 0});
     }
   return ops;
@@ -534,6 +535,17 @@ struct Exec {
     const Dims &d = D();
     hipStream_t s = overlap ? c->ss : cst(sb);
     if (overlap) HIPX(hipStreamWaitEvent(s, c->evBdX[l * 2 + sb], 0));
+    // OVERLAP_STREAMS cool-down: the step's last AllReduce point, C(B) of
+    // layer 0 for sub-batch 1, goes to sub-batch 0's stream, which has issued
+    // all of its own work by then, so that it runs beside sub-batch 1's
+    // weight-gradient GEMMs instead of ahead of them on one stream.  Its
+    // input is ready once sub-batch 1's dX GEMM is (evBdX carries no other
+    // edge in this mode); the step's closing join waits for both streams.
+    if (by_sb && l == 0 && sb == 1) {
+      HIPX(hipEventRecord(c->evBdX[1], c->ss));
+      HIPX(hipStreamWaitEvent(c->cs, c->evBdX[1], 0));
+      s = c->cs;
+    }
     if (!d.full) {
       if (int r = sum(ws() + W.dxo[sb], d.w > 1 ? peers(c->buf.peers_bwd, l, sb) : nullptr, grad_in(l, sb), s))
         return r;

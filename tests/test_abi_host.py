@@ -170,7 +170,11 @@ def test_op_lists_match_oracle_schedules(n_layers):
         assert ctx.schedule_ops(mode) == oschedule.build_ops(n_layers, mode), mode
     # the fused overlap runs the overlapped op list (sums on the next GEMM launch)
     assert ctx.schedule_ops("overlap_fused") == oschedule.build_ops(n_layers, "overlap_fine")
-    # one stream per sub-batch: the same ops in the same order, stream = sub-batch
-    by_sb = [(k, l, sb, sb) for (k, l, sb, _) in oschedule.build_ops(n_layers, "overlap_fine")]
+    # one stream per sub-batch: the same ops in the same order, stream =
+    # sub-batch, except the step's last AllReduce point (C(B) of layer 0,
+    # sub-batch 1), which runs on sub-batch 0's stream beside sub-batch 1's
+    # weight-gradient GEMMs
+    by_sb = [(k, l, sb, 0 if (k, l) == ("C_B", 0) else sb)
+             for (k, l, sb, _) in oschedule.build_ops(n_layers, "overlap_fine")]
     assert ctx.schedule_ops("overlap_streams") == by_sb
     ctx.close()
