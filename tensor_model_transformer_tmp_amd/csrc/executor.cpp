@@ -178,7 +178,14 @@ int check_config(const oases_config *cfg, Dims *D, std::string *err) {
   return OASES_OK;
 }
 
-std::vector<Op> build_ops(int L, int mode) {
+// OVERLAP_STREAMS cool-down (Exec::cooldown): sub-batch 1's last weight
+// gradients move to sub-batch 0's stream when the step's last AllReduce point
+// outlasts the cross-queue wait the move puts on the step's critical path.
+// Measured: the 4096- and 8192-hidden pairs (128 and 256 MiB of sum inputs)
+// 1% faster, the 1024-hidden pair (16 MiB) 2% slower.
+bool cooldown_move(const Dims &d) { return (int64_t)d.T * d.h * d.w * (int64_t)d.esz >= ((int64_t)64 << 20); }
+
+std::vector<Op> build_ops(int L, int mode, bool cool) {
   std::vector<Op> ops;
   const int side = (mode == OASES_OVERLAP_FINE || mode == OASES_OVERLAP_FUSED) ? 1 : 0;
   const bool by_sb = mode == OASES_OVERLAP_STREAMS;  // stream = sub-batch
@@ -192,9 +199,8 @@ std::vector<Op> build_ops(int L, int mode) {
       if (mode != OASES_SERIAL_NO_RECOMPUTE) ops.push_back({OP_R, l, sb, by_sb ? sb : 0});
       if (mode == OASES_SERIAL_DEFAULT_RECOMPUTE) ops.push_back({OP_CR, l, sb, 0});
       ops.push_back({OP_BDX, l, sb, by_sb ? sb : 0});
-      // by sub-batch: the step's last C(B) runs on sub-batch 0's stream (op_CB)
-      ops.push_back({OP_CB, l, sb, by_sb ? (l == 0 ? 0 : sb) : side});
-      ops.push_back({OP_BDW, l, sb, by_sb ? sb : 0});
+      ops.push_back({OP_CB, l, sb, by_sb ? sb : side});
+      ops.push_back({OP_BDW, l, sb, by_sb ? (cool && l == 0 ? 0 : sb) : 0});
     }
   return ops;
 }
@@ -262,8 +268,9 @@ struct oases_ctx {
   std::vector<hipEvent_t> evF, evCF, evBdX, evCB;
   // OVERLAP_STREAMS: sub-batch 0's dW_in and db_in of layer l done [l], its
   // LayerNorm weight gradients done [L + l], fork (after sub-batch 0's first
-  // column GEMM) [2L], join [2L + 1], its
-  // dW_out of layer l done [2L + 2 + l]
+  // column GEMM) [2L], join [2L + 1], its dW_out of layer l done [2L + 2 + l];
+  // cool-down: sub-batch 1's layer-0 dW_out operands ready [3L + 2], its
+  // layer-0 dX GEMM done [3L + 3]
   std::vector<hipEvent_t> evSB;
   hipGraphExec_t gexec[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   std::vector<uint8_t> fwd_done, bwd_done;
@@ -307,6 +314,12 @@ struct Exec {
   // points) on the side stream, of sub-batch 0 on the compute stream
   bool by_sb = false;
   hipStream_t cst(int sb) const { return by_sb && sb == 1 ? c->ss : c->cs; }
+  // OVERLAP_STREAMS cool-down: sub-batch 1's B_dW of layer 0 runs on sub-batch
+  // 0's stream, which has issued all of its own work by then.  dW_out runs
+  // beside sub-batch 1's dX GEMM, dW_in beside its last AllReduce point
+  // (instead of all three after one another on one stream), and both follow
+  // sub-batch 0's weight gradients on that stream, the accumulation order.
+  bool cooldown(int l, int sb) const { return by_sb && l == 0 && sb == 1 && cooldown_move(D()); }
   // OVERLAP_FUSED (bf16): an AllReduce point waits here and runs as extra
   // workgroups of the next GEMM launched on the compute stream
   bool fused = false;
@@ -504,6 +517,7 @@ struct Exec {
     const void *dy = dP(l, sb);
     if (d.full)  // the AllReduce inputs' gradient: dropout backward of dY (Eq. (1))
       HIPX(dropout_bwd(grad_out(l, sb), ws() + W.dS[sb], (int64_t)d.T * d.h, tail(l, sb), cst(sb)));
+    if (cooldown(l, sb)) HIPX(hipEventRecord(c->evSB[3 * d.L + 2], cst(sb)));  // dY and R's activations
     char *dpre = ws() + W.dpre[sb];
     if (d.blocks[l] == OASES_FFN) {
       GemmArgs g{};  // dU = (dY W_out) * gelu'(U)
@@ -529,23 +543,13 @@ struct Exec {
     g.C = ws() + W.dxo[sb]; g.ldc = d.h;
     if (int r = gemm(KC_GEMM_DX, KC, MC, EPI_STORE, g, cst(sb))) return r;
     if (overlap) HIPX(hipEventRecord(c->evBdX[l * 2 + sb], cst(sb)));
+    if (cooldown(l, sb)) HIPX(hipEventRecord(c->evSB[3 * d.L + 3], cst(sb)));  // dpre and dX_own
     return OASES_OK;
   }
   int op_CB(int l, int sb) {
     const Dims &d = D();
     hipStream_t s = overlap ? c->ss : cst(sb);
     if (overlap) HIPX(hipStreamWaitEvent(s, c->evBdX[l * 2 + sb], 0));
-    // OVERLAP_STREAMS cool-down: the step's last AllReduce point, C(B) of
-    // layer 0 for sub-batch 1, goes to sub-batch 0's stream, which has issued
-    // all of its own work by then, so that it runs beside sub-batch 1's
-    // weight-gradient GEMMs instead of ahead of them on one stream.  Its
-    // input is ready once sub-batch 1's dX GEMM is (evBdX carries no other
-    // edge in this mode); the step's closing join waits for both streams.
-    if (by_sb && l == 0 && sb == 1) {
-      HIPX(hipEventRecord(c->evBdX[1], c->ss));
-      HIPX(hipStreamWaitEvent(c->cs, c->evBdX[1], 0));
-      s = c->cs;
-    }
     if (!d.full) {
       if (int r = sum(ws() + W.dxo[sb], d.w > 1 ? peers(c->buf.peers_bwd, l, sb) : nullptr, grad_in(l, sb), s))
         return r;
@@ -588,25 +592,31 @@ struct Exec {
     g.C = p.dw_out; g.ldc = nmid; g.beta = sb;
     // with a stream per sub-batch, sub-batch 1 adds into each weight gradient
     // once sub-batch 0 has written it: its dW_out GEMM waits for sub-batch 0's
-    // dW_out only, and so runs beside sub-batch 0's dW_in GEMM
+    // dW_out only, and so runs beside sub-batch 0's dW_in GEMM.  In the
+    // cool-down both GEMMs follow sub-batch 0's on its stream, and wait for
+    // their operands from sub-batch 1's stream instead.
     const int L = d.L;
-    if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(c->ss, c->evSB[2 * L + 2 + l], 0));
-    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g, cst(sb))) return r;
+    const bool cool = cooldown(l, sb);
+    hipStream_t s = cool ? c->cs : cst(sb);
+    if (cool) HIPX(hipStreamWaitEvent(s, c->evSB[3 * L + 2], 0));
+    else if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(s, c->evSB[2 * L + 2 + l], 0));
+    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g, s)) return r;
     if (by_sb && sb == 0) HIPX(hipEventRecord(c->evSB[2 * L + 2 + l], c->cs));
-    if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(c->ss, c->evSB[l], 0));  // dW_in and db_in
+    if (cool) HIPX(hipStreamWaitEvent(s, c->evSB[3 * L + 3], 0));  // dpre
+    else if (by_sb && sb == 1) HIPX(hipStreamWaitEvent(s, c->evSB[l], 0));  // dW_in and db_in
     GemmArgs g2{};  // dW_in[nin, h] (+)= dpre^T X
     g2.M = nin; g2.N = d.h; g2.K = d.T;
     g2.A = dpre; g2.lda = nin; g2.B = gemm_in(l, sb); g2.ldb = d.h;
     g2.C = p.dw_in; g2.ldc = d.h; g2.beta = sb;
     if (bf16()) {  // db_in (+)= column sums of dpre, computed by the same GEMM
       g2.colsum = static_cast<float *>(p.db_in);
-      return gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, cst(sb));
+      return gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, s);
     }
-    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, cst(sb))) return r;
-    if (int r = prof_begin(KC_COLSUM, cst(sb))) return r;
+    if (int r = gemm(KC_GEMM_DW, MC, MC, EPI_F32, g2, s)) return r;
+    if (int r = prof_begin(KC_COLSUM, s)) return r;
     HIPX(colsum(bf16(), dpre, d.T, nin, nin, reinterpret_cast<float *>(ws() + W.colsum[sb]),
-                static_cast<float *>(p.db_in), sb, cst(sb)));
-    return prof_end(KC_COLSUM, cst(sb));
+                static_cast<float *>(p.db_in), sb, s));
+    return prof_end(KC_COLSUM, s);
   }
 
   int run(const Op &o) {
@@ -638,7 +648,7 @@ int Exec::gemm(int cls, oases::Layout la, oases::Layout lb, Epi epi, const GemmA
 int ensure_events(oases_ctx *c) {
   if (!c->evF.empty()) return OASES_OK;
   const int n = c->D.L * 2;
-  c->evSB.resize(n + 2 + c->D.L, nullptr);
+  c->evSB.resize(n + 4 + c->D.L, nullptr);
   for (auto *v : {&c->evF, &c->evCF, &c->evBdX, &c->evCB, &c->evSB}) {
     if (v != &c->evSB) v->resize(n, nullptr);
     // device-internal ordering only: no timing, no system-scope fence
@@ -809,7 +819,7 @@ int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph) {
   if (!c) return OASES_E_ARG;
   if (mode < 0 || mode > 5) return set_err(c, OASES_E_ARG, "bad mode");
   if (int r = need_ready(c, mode)) return r;
-  const std::vector<Op> ops = build_ops(c->D.L, mode);
+  const std::vector<Op> ops = build_ops(c->D.L, mode, cooldown_move(c->D));
   std::fill(c->fwd_done.begin(), c->fwd_done.end(), 0);
   std::fill(c->bwd_done.begin(), c->bwd_done.end(), 0);
   if (!use_graph) return issue_ops(c, mode, ops);
@@ -837,7 +847,7 @@ int schedule_step(oases_ctx *c, int32_t mode, int32_t use_graph) {
 int oases_schedule_ops(const oases_ctx *c, int32_t mode, int32_t *ops, int32_t cap, int32_t *n_ops) {
   if (!c || !n_ops || (cap > 0 && !ops) || cap < 0) return OASES_E_ARG;
   if (mode < 0 || mode > 5) return OASES_E_ARG;
-  const std::vector<Op> v = build_ops(c->D.L, mode);
+  const std::vector<Op> v = build_ops(c->D.L, mode, cooldown_move(c->D));
   *n_ops = (int32_t)v.size();
   for (int i = 0; i < (int)v.size() && i < cap; ++i) {
     ops[4 * i + 0] = v[i].kind; ops[4 * i + 1] = v[i].layer;

@@ -171,10 +171,25 @@ def test_op_lists_match_oracle_schedules(n_layers):
     # the fused overlap runs the overlapped op list (sums on the next GEMM launch)
     assert ctx.schedule_ops("overlap_fused") == oschedule.build_ops(n_layers, "overlap_fine")
     # one stream per sub-batch: the same ops in the same order, stream =
-    # sub-batch, except the step's last AllReduce point (C(B) of layer 0,
-    # sub-batch 1), which runs on sub-batch 0's stream beside sub-batch 1's
-    # weight-gradient GEMMs
-    by_sb = [(k, l, sb, 0 if (k, l) == ("C_B", 0) else sb)
-             for (k, l, sb, _) in oschedule.build_ops(n_layers, "overlap_fine")]
+    # sub-batch (at this size, 16 MiB of AllReduce-point inputs, the
+    # cool-down keeps every op on its sub-batch's stream)
+    by_sb = [(k, l, sb, sb) for (k, l, sb, _) in oschedule.build_ops(n_layers, "overlap_fine")]
     assert ctx.schedule_ops("overlap_streams") == by_sb
+    ctx.close()
+
+
+@pytest.mark.parametrize("preset,moved", [("c2_pair_h1024", False), ("c3_pair_h4096", True),
+                                          ("c4_stack8_h2048", True), ("c5_pair_h8192", True),
+                                          ("c1_ffn_fp32", False)])
+def test_cooldown_stream_of_last_weight_gradients(preset, moved):
+    """Sub-batch streams: from 64 MiB of AllReduce-point inputs up, sub-batch
+    1's last weight gradients (B_dW of layer 0) run on sub-batch 0's stream."""
+    cfg = gen.PRESETS[preset]
+    ctx = shard.ShardContext(cfg)
+    ops = ctx.schedule_ops("overlap_streams")
+    want = [(k, l, sb, 0 if moved and (k, l) == ("B_dW", 0) else sb)
+            for (k, l, sb, _) in oschedule.build_ops(cfg.n_layers, "overlap_fine")]
+    assert ops == want
+    # the other modes never move it
+    assert ctx.schedule_ops("overlap_fine") == oschedule.build_ops(cfg.n_layers, "overlap_fine")
     ctx.close()
