@@ -87,9 +87,11 @@ typedef enum { OASES_ATTN = 0, OASES_FFN = 1 } oases_block;
  * sub-batch 1's on the side stream, so each sub-batch's sums and kernels run
  * beside the other's; the only cross-stream edges order the two
  * sub-batches' weight-gradient accumulation (and a fork and join per step),
- * except in the cool-down: sub-batch 1's last weight gradients (B_dW of
+ * except in the cool-down: from 64 MiB of AllReduce-point inputs
+ * (T_sb * h * w elements) up, sub-batch 1's last weight gradients (B_dW of
  * layer 0) run on the compute stream, after sub-batch 0's, so that they
- * overlap sub-batch 1's dX GEMM and its last AllReduce point.
+ * overlap sub-batch 1's dX GEMM and its last AllReduce point
+ * (oases_schedule_ops reports that stream).
  * All modes give bit-identical results. */
 typedef enum {
   OASES_OVERLAP_FINE = 0,
