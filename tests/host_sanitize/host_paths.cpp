@@ -146,6 +146,28 @@ int main() {
   oases_destroy(ctx);
   oases_destroy(nullptr);
 
+  // ---- sub-batch streams cool-down: from 64 MiB of AllReduce-point inputs
+  // up, sub-batch 1's B_dW of layer 0 is listed on the compute stream (0) ----
+  for (int big = 0; big < 2; ++big) {
+    oases_config b = pair_config(pair, 2);
+    if (big) {  // the 8192-hidden pair shard: 2048 x 8192 x 8 bf16 = 256 MiB per point
+      b.micro_batch = 2; b.seq = 2048; b.hidden = 8192; b.heads_per_shard = 8; b.head_dim = 128;
+      b.ffn_shard = 4096; b.tmp_width = 8;
+    }
+    oases_ctx *cx = nullptr;
+    EXPECT(oases_create(&b, &cx) == OASES_OK);
+    if (!cx) continue;
+    int32_t n = 0;
+    EXPECT(oases_schedule_ops(cx, OASES_OVERLAP_STREAMS, nullptr, 0, &n) == OASES_OK);
+    std::vector<int32_t> ops(4 * (size_t)n);
+    EXPECT(oases_schedule_ops(cx, OASES_OVERLAP_STREAMS, ops.data(), n, &n) == OASES_OK);
+    for (int i = 0; i < n; ++i) {
+      const int k = ops[4 * i], l = ops[4 * i + 1], sb = ops[4 * i + 2], st = ops[4 * i + 3];
+      EXPECT(st == ((big && k == 6 && l == 0) ? 0 : sb));
+    }
+    oases_destroy(cx);
+  }
+
   // ---- context-free entry points: argument checks (no launch) ----
   size_t need = 0;
   EXPECT(oases_attention_bwd_workspace_bytes(2, 100, 3, &need) == OASES_OK && need > 0);
