@@ -123,6 +123,43 @@ def test_schedules_bit_identical(name):
     dev.close()
 
 
+# sub-batch streams cool-down: from 64 MiB of AllReduce-point inputs
+# (T_sb * h * w elements in the storage type) up, sub-batch 1's last weight
+# gradients run on sub-batch 0's stream; sized to exactly that much, with
+# small blocks around it (float32: FFN only, its column sums by their own kernel)
+COOLDOWN = {
+    "cool_pair_bf16": gen.ShardConfig(name="cool_pair_bf16", blocks=(gen.ATTN, gen.FFN), micro_batch=2,
+                                      seq=1024, hidden=4096, heads_per_shard=1, head_dim=64, ffn_shard=256,
+                                      tmp_width=8, dtype=gen.BF16, seed=15),
+    "cool_ffn_fp32": gen.ShardConfig(name="cool_ffn_fp32", blocks=(gen.FFN,), micro_batch=2, seq=1024,
+                                     hidden=4096, heads_per_shard=1, head_dim=64, ffn_shard=256,
+                                     tmp_width=4, dtype=gen.F32, seed=16),
+}
+
+
+@pytest.mark.parametrize("name", list(COOLDOWN))
+def test_cooldown_schedule_matches_oracle_and_serial(name):
+    """The sub-batch-streams schedule with its cool-down (sub-batch 1's layer-0
+    weight gradients on sub-batch 0's stream) against the oracle, and bit for
+    bit against the serial schedule, eagerly and as hipGraph replays."""
+    cfg = COOLDOWN[name]
+    esz = 2 if cfg.dtype == gen.BF16 else 4
+    assert (cfg.micro_batch // 2) * cfg.seq * cfg.hidden * cfg.tmp_width * esz >= 64 << 20
+    inp = gen.make_inputs(cfg)
+    ref = oschedule.run_step(inp, "serial_fine")
+    dev = DeviceShard(inp, modes=("overlap_streams", "serial_fine"))
+    ops = dev.ctx.schedule_ops("overlap_streams")
+    assert ("B_dW", 0, 1, 0) in ops  # the cool-down path is the one taken
+    dev.step("serial_fine")
+    base = dev.results()
+    _compare(cfg, base, ref, 2e-2 if cfg.dtype == gen.BF16 else 1e-5)
+    for graph in (False, True):
+        for _ in range(2):  # graph: first call captures, second replays
+            dev.step("overlap_streams", use_graph=graph)
+            _bitwise_equal(dev.results(), base)
+    dev.close()
+
+
 def test_layer_entry_points_match_schedule_step():
     cfg = SMALL["stack4_d64"]
     inp = gen.make_inputs(cfg)
